@@ -1,0 +1,15 @@
+"""CPU fp64 oracle for the fused MHA forward.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product path must not.
+"""
+from .attention import (  # noqa: F401
+    attention_fwd,
+    attention_fwd_bruteforce,
+    attention_probs,
+    causal_visible,
+    scores,
+    softmax_rows,
+    weighted_values,
+    log_sum_exp,
+)
