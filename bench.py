@@ -1,0 +1,220 @@
+"""Benchmark of the fused MHA forward on one MI355X.
+
+A step is one mha_fwd call over the whole workload (inputs already resident
+in HBM). Default workload: B=1, H=8, Nq=Nk=16384, d=128, bf16, causal (the
+long-sequence small-batch regime of the FlashAttention long-sequence post).
+Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+                  [--no-cpu-baseline] [--cpu-seconds S] [--calib-copy-mib M]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak (B=1,H=8,N=16k,d=128 causal)"
+PEAK_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 MFMA peak
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "head_attention_mha_amd", "csrc", "mha_fwd_kernel.hpp"),
+    os.path.join(ROOT, "head_attention_mha_amd", "csrc", "mha_api.hip"),
+]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def hbm_traffic(workload: str):
+    """Per-launch HBM bytes (FETCH + WRITE) from the committed counter summary,
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_device(torch, bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
+
+
+def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float) -> dict:
+    """The fp64 oracle, as it stands, on evenly spaced query rows of every head."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
+                      if i.get("user_api") == "blas") or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, k, v = (wl.bits_to_f64(x, w.dtype) for x in (qb, kb, vb))
+
+    def timed(rows):
+        t0 = time.perf_counter()
+        oracle.attention_fwd(q, k, v, w.causal, w.scale, rows=rows)
+        return time.perf_counter() - t0
+
+    pilot = np.unique(np.linspace(0, w.Nq - 1, 16).astype(np.int64))
+    t_p = max(timed(pilot), 1e-6)
+    n = int(min(w.Nq, max(16, len(pilot) * target_s / t_p)))
+    rows = np.unique(np.linspace(0, w.Nq - 1, n).astype(np.int64))
+    t = timed(rows)
+    vis = (rows + 1).clip(max=w.Nk) if w.causal else np.full(len(rows), w.Nk)
+    flops = 4.0 * w.d * float(vis.sum()) * w.B * w.H
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(rows)} evenly spaced query rows of each of the {w.B * w.H} heads "
+                   f"({len(rows) / w.Nq:.1%} of the rows, all their keys), fp64 NumPy, "
+                   f"{t:.1f} s; FLOPs counted as 4*d*visible keys per row"),
+        "seconds": t,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_causal", choices=list(wl.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards over heads with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import head_attention_mha_amd as mha
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU available", file=sys.stderr)
+        return 1
+    mha.load_library()
+    w = wl.WORKLOADS[args.workload]
+    qb, kb, vb = wl.make_inputs(w)
+    q, k, v = (to_device(torch, x, w.dtype) for x in (qb, kb, vb))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    dt = mha.MHA_DTYPE_BF16 if w.dtype == "bf16" else mha.MHA_DTYPE_FP16
+    argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            w.B, w.H, w.Nq, w.Nk, w.d, int(w.causal), w.scale, sp, dt)
+
+    def step():
+        st = mha.mha_fwd(*argv)
+        if st != mha.MHA_OK:
+            raise mha.MhaError(st)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=q.device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"calibration copy: {n * 2} bytes read, {n * 2} bytes written per launch",
+              file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: events on the stream the kernel is launched on
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])  # ms
+    total_ms = ev[0].elapsed_time(ev[K])
+    ms_per_step = total_ms / K
+
+    flops = w.flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (per.mean() * 1e-3) / 1e12
+    traffic = hbm_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "io_dtype": w.dtype, "accumulate": "fp32",
+                   "flops_per_step": flops},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "mha_fwd_kernel",
+            "launch_ms": {"mean": round(float(per.mean()), 5), "median": round(float(np.median(per)), 5),
+                          "min": round(float(per.min()), 5)},
+        },
+        "timed_wall_s": round(wall, 3),
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
+              flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

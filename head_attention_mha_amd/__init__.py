@@ -1,0 +1,22 @@
+"""Fused multi-head attention forward for AMD MI355X (gfx950).
+
+The computation lives in the HIP library ``libmha.so`` behind the C ABI of
+include/mha.h; this package only binds it (see ``_binding``).
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    LIB_PATH,
+    MHA_DTYPE_BF16,
+    MHA_DTYPE_FP16,
+    MHA_ERR_DEVICE,
+    MHA_ERR_INVALID_ARG,
+    MHA_ERR_LAUNCH,
+    MHA_ERR_UNSUPPORTED,
+    MHA_OK,
+    MhaError,
+    attention,
+    load_library,
+    mha_abi_version,
+    mha_fwd,
+    mha_status_string,
+)

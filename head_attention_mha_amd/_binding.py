@@ -1,0 +1,118 @@
+"""ctypes binding of libmha.so (argument marshalling only).
+
+The names follow include/mha.h. ``mha_fwd`` takes raw device pointers and
+sizes exactly like the C entry point; ``attention`` is a convenience wrapper
+that takes PyTorch device tensors, allocates O and LSE with PyTorch and calls
+``mha_fwd`` on the current stream. Every step of the computation runs in the
+HIP kernel; if the library is missing this module raises instead of
+computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmha.so")
+
+MHA_OK = 0
+MHA_ERR_INVALID_ARG = 1
+MHA_ERR_UNSUPPORTED = 2
+MHA_ERR_DEVICE = 3
+MHA_ERR_LAUNCH = 4
+MHA_DTYPE_FP16 = 0
+MHA_DTYPE_BF16 = 1
+
+# Every symbol include/mha.h declares.
+EXPORTED_SYMBOLS = ("mha_fwd", "mha_status_string", "mha_abi_version")
+
+_lib = None
+
+
+class MhaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"mha_fwd failed: {mha_status_string(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmha.so once. Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m head_attention_mha_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    lib.mha_fwd.restype = ctypes.c_int
+    lib.mha_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+    ]
+    lib.mha_status_string.restype = ctypes.c_char_p
+    lib.mha_status_string.argtypes = [ctypes.c_int]
+    lib.mha_abi_version.restype = ctypes.c_int
+    lib.mha_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def mha_status_string(status: int) -> str:
+    return load_library().mha_status_string(int(status)).decode()
+
+
+def mha_abi_version() -> int:
+    return int(load_library().mha_abi_version())
+
+
+def mha_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int, d: int,
+            causal: int, scale: float, stream: int | None, dtype: int) -> int:
+    """Call the C entry point with raw pointers; returns the status code."""
+    return int(load_library().mha_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal),
+                                      float(scale), stream, int(dtype)))
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+              stream=None):
+    """O, LSE = attention(Q, K, V) for PyTorch device tensors.
+
+    q: [B, Nq, H, d], k and v: [B, Nk, H, d], contiguous, one dtype
+    (float16 or bfloat16), on a HIP device. Returns (o [B, Nq, H, d] in the
+    input dtype, lse [B, H, Nq] float32). ``scale`` defaults to 1/sqrt(d).
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, N, H, d]")
+    B, Nq, H, d = q.shape
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    Nk = k.shape[1]
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one GPU device")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    dt = MHA_DTYPE_BF16 if q.dtype == torch.bfloat16 else MHA_DTYPE_FP16
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = mha_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, Nq, Nk, d, int(bool(causal)), float(scale), stream, dt)
+    if st != MHA_OK:
+        raise MhaError(st)
+    return out, lse

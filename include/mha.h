@@ -1,0 +1,98 @@
+/*
+ * mha.h -- C ABI of the fused multi-head attention forward for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The operation (per batch b and head h) is
+ *
+ *     O = softmax(scale * Q K^T  [+ causal mask]) V
+ *     LSE_i = ln( sum_j exp(scale * q_i . k_j) )   over the visible keys j
+ *
+ * - the attention formula: "CANN ops-transformer" article, section 1 (the MHA
+ *   formula softmax(QK^T / sqrt(d_k)) V), and "SparkAttention", MHA-Forward
+ *   passage (Eq. 1: per head, heads split the embedding);
+ * - the fused, tiled evaluation that never writes the Nq x Nk score matrix to
+ *   memory and writes O once: "SparkAttention", Fig. 6 passage (steps 1-4 and
+ *   the final write-back), and the FlashAttention long-sequence post,
+ *   "Attention parallelism" (row blocks per worker);
+ * - LSE = m + log l with m the running row max and l the running row sum:
+ *   "StreamKL", Methodology section 1 (online formulation) and section 2 (the
+ *   stored LSE from which P = exp(S - LSE) is regenerated);
+ * - causal: key j is visible to query i iff j <= i (top-left aligned, also
+ *   when Nq != Nk): "SparkAttention", Transformer data-flow passage (Fig. 1),
+ *   the masked decoder attention, read inclusively. Whole key tiles past the
+ *   causal frontier are skipped: "StreamKL", Methodology section 1.
+ */
+#ifndef MHA_MI355X_H
+#define MHA_MI355X_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+  MHA_OK = 0,
+  MHA_ERR_INVALID_ARG = 1, /* a null/misaligned/overlapping pointer, a bad size, flag or scale */
+  MHA_ERR_UNSUPPORTED = 2, /* valid but not implemented: head dim other than 64/128, device not gfx950 */
+  MHA_ERR_DEVICE = 3,      /* no usable HIP device (e.g. a host without a GPU) */
+  MHA_ERR_LAUNCH = 4       /* the kernel launch itself failed */
+} mha_status_t;
+
+/* Element type of Q, K, V and O (LSE is always fp32). */
+typedef enum { MHA_DTYPE_FP16 = 0, MHA_DTYPE_BF16 = 1 } mha_dtype_t;
+
+/*
+ * mha_fwd -- fused attention forward: writes O and LSE.
+ *
+ * Arguments
+ *   q      device pointer, [B, Nq, H, d] row-major, element type `dtype`
+ *   k, v   device pointers, [B, Nk, H, d] row-major, element type `dtype`
+ *   o      device pointer, [B, Nq, H, d] row-major, element type `dtype`
+ *          (written; each element is the fp32 result rounded to nearest even)
+ *   lse    device pointer, [B, H, Nq] fp32 (written; natural log)
+ *   B, H   batch size and number of heads, >= 0
+ *   Nq, Nk query and key/value sequence lengths, >= 0; Nk >= 1 whenever
+ *          B*H*Nq > 0 (a softmax over no keys is undefined)
+ *   d      head dimension: 64 or 128
+ *   causal 0 or 1 (1: key j visible to query i iff j <= i)
+ *   scale  softmax scale applied to q.k, finite and > 0 (typically 1/sqrt(d))
+ *   stream hipStream_t to enqueue on, passed as void*; NULL = default stream
+ *   dtype  MHA_DTYPE_FP16 or MHA_DTYPE_BF16
+ *
+ * Layout: the [S, H*D] per-sequence layout of the CANN article, section 1,
+ * with a leading batch dimension; no strides other than these.
+ *
+ * Ownership and execution: every pointer belongs to the caller and must stay
+ * valid until the enqueued work completes. The library allocates nothing,
+ * keeps no workspace and retains no pointer. q, k and v are only read; o and
+ * lse are overwritten entirely. The call enqueues one kernel on `stream` and
+ * returns without synchronising. It is reentrant; calls on one stream run in
+ * order, calls on different streams that write the same o/lse race.
+ *
+ * Requirements checked before anything is enqueued (violations return
+ * MHA_ERR_INVALID_ARG and write nothing): q, k, v, o non-null and 16-byte
+ * aligned, lse non-null and 4-byte aligned (null is accepted only for a
+ * tensor with zero elements); o and lse must not overlap each other or any
+ * input. An empty problem (B*H*Nq == 0) returns MHA_OK and enqueues nothing.
+ *
+ * Errors are reported only through the return value: nothing is printed,
+ * nothing aborts, no C++ exception crosses this boundary. A fault inside the
+ * kernel (e.g. a pointer to too small a buffer) surfaces at the caller's next
+ * synchronisation of `stream`.
+ */
+mha_status_t mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                     void* stream, int dtype);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* mha_status_string(int status);
+
+/* ABI version of this header; bumped on any incompatible change. */
+#define MHA_ABI_VERSION 1
+int mha_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_MI355X_H */

@@ -1,0 +1,269 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the
+GPU. Every workload at full size (sampled rows for the two long causal ones,
+all rows otherwise), ragged and edge shapes, and the closed-form invariants
+evaluated on the kernel itself."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from parity import assert_parity, compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    # name the case on the real stderr before any GPU work, so a run that
+    # dies mid-test still says which case it was
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+@pytest.fixture(scope="module")
+def mha(torch_mod):
+    import head_attention_mha_amd as m
+    m.load_library()
+    return m
+
+
+def to_dev(torch, bits: np.ndarray, dtype: str):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    t = t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    return t.cuda()
+
+
+def to_bits(t) -> np.ndarray:
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run(torch, mha, qb, kb, vb, dtype, causal, scale, prefill_nan=True):
+    q, k, v = (to_dev(torch, x, dtype) for x in (qb, kb, vb))
+    o = torch.empty_like(q)
+    B, Nq, H, d = q.shape
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if prefill_nan:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    mha.attention(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    return to_bits(o), lse.cpu().numpy()
+
+
+def sample_rows(Nq: int, seed: int = 0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(Nq, 40)))
+    rows |= set(range(max(0, Nq - 16), Nq))
+    for t in (64, 127, 128, 129, 255, 256, 1023, 1024, Nq // 2, Nq // 2 + 1):
+        if 0 <= t < Nq:
+            rows.add(t)
+    rows |= set(rng.choice(Nq, size=min(Nq, 120), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def check_against_oracle(torch, mha, qb, kb, vb, dtype, causal, scale, rows=None, label=""):
+    o_bits, lse = run(torch, mha, qb, kb, vb, dtype, causal, scale)
+    # every output element was written and is finite (NaN prefill)
+    assert np.all(np.isfinite(wl.bits_to_f32(o_bits, dtype))), f"{label}: unwritten/non-finite O"
+    assert np.all(np.isfinite(lse)), f"{label}: unwritten/non-finite LSE"
+    q, k, v = (wl.bits_to_f64(x, dtype) for x in (qb, kb, vb))
+    O_ref, L_ref = oracle.attention_fwd(q, k, v, causal, scale, rows=rows)
+    if rows is not None:
+        o_bits = o_bits[:, rows]
+        lse = lse[:, :, rows]
+    st = compare(o_bits, lse, O_ref, L_ref, dtype)
+    sys.__stderr__.write(f"[parity] {label}: {st}\n")
+    assert_parity(st, label)
+    return st
+
+
+# ------------------------------------------------------------ the workloads
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_workload_parity(torch_mod, mha, name):
+    w = wl.WORKLOADS[name]
+    qb, kb, vb = wl.make_inputs(w)
+    rows = sample_rows(w.Nq) if w.Nq * w.Nk * w.B * w.H > 2**31 else None
+    check_against_oracle(torch_mod, mha, qb, kb, vb, w.dtype, w.causal, w.scale, rows, name)
+
+
+# -------------------------------------------------------------- edge shapes
+EDGE = [
+    # B, H, Nq, Nk, d, dtype, causal
+    (1, 1, 1, 1, 64, "fp16", False),
+    (1, 1, 1, 1, 128, "bf16", True),
+    (2, 3, 77, 131, 64, "bf16", False),
+    (2, 3, 77, 131, 128, "fp16", True),
+    (1, 2, 131, 77, 64, "fp16", True),     # Nq > Nk, causal, top-left
+    (1, 2, 131, 77, 128, "bf16", False),
+    (1, 1, 129, 129, 128, "bf16", True),   # one row past a query tile
+    (1, 2, 200, 1, 64, "fp16", False),     # a single key
+    (1, 2, 1, 300, 128, "bf16", False),    # a single query
+    (3, 1, 63, 65, 64, "bf16", True),
+    (1, 4, 256, 256, 128, "fp16", True),
+    (1, 1, 513, 1000, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "B{}H{}q{}k{}d{}{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], "c" if c[6] else ""))
+def test_edge_shapes(torch_mod, mha, case):
+    B, H, Nq, Nk, d, dtype, causal = case
+    qb, kb, vb = wl.random_inputs(B, H, Nq, Nk, d, dtype, seed=100 + Nq + Nk)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    check_against_oracle(torch_mod, mha, qb, kb, vb, dtype, causal, scale, None, str(case))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_peaky_scores(torch_mod, mha, dtype):
+    """Large score spread (std 3 inputs, scale 1): exercises the running-max
+    rescaling far from the uniform regime."""
+    qb, kb, vb = wl.random_inputs(1, 2, 300, 700, 64, dtype, seed=9, std=1.0)
+    qb2, kb2, _ = wl.random_inputs(1, 2, 300, 700, 64, dtype, seed=10, std=3.0)
+    check_against_oracle(torch_mod, mha, qb2, kb2, vb, dtype, True, 0.25, None, f"peaky-{dtype}")
+
+
+# ------------------------------------------------ closed forms on the kernel
+def _bits(x, dtype):
+    return wl.round_bits(np.asarray(x, np.float32), dtype)
+
+
+@pytest.mark.parametrize("d,dtype,causal", [(64, "fp16", False), (128, "bf16", True)])
+def test_ones_v_gives_ones(torch_mod, mha, d, dtype, causal):
+    B, H, N = 1, 2, 300
+    qb, kb, _ = wl.random_inputs(B, H, N, N, d, dtype, seed=21)
+    vb = _bits(np.ones((B, N, H, d)), dtype)
+    o_bits, lse = run(torch_mod, mha, qb, kb, vb, dtype, causal, 1 / math.sqrt(d))
+    O = wl.bits_to_f64(o_bits, dtype)
+    assert np.abs(O - 1).max() <= 1e-3
+
+
+@pytest.mark.parametrize("d,dtype,causal", [(64, "bf16", True), (128, "fp16", False)])
+def test_zero_q_gives_column_means(torch_mod, mha, d, dtype, causal):
+    B, H, N = 1, 2, 257
+    _, kb, vb = wl.random_inputs(B, H, N, N, d, dtype, seed=22)
+    qb = _bits(np.zeros((B, N, H, d)), dtype)
+    o_bits, lse = run(torch_mod, mha, qb, kb, vb, dtype, causal, 0.1)
+    O = wl.bits_to_f64(o_bits, dtype)
+    v = wl.bits_to_f64(vb, dtype)
+    if causal:
+        want = np.cumsum(v, axis=1) / np.arange(1, N + 1)[None, :, None, None]
+        want_lse = np.log(np.arange(1, N + 1))[None, None, :]
+    else:
+        want = np.broadcast_to(v.mean(axis=1, keepdims=True), v.shape)
+        want_lse = np.full((1, 1, N), math.log(N))
+    assert np.abs(O - want).max() <= 1e-2
+    assert np.abs(lse - want_lse).max() <= 1e-3
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "fp16"), (128, "bf16")])
+def test_causal_row0_is_v0(torch_mod, mha, d, dtype):
+    B, H, N = 2, 3, 150
+    qb, kb, vb = wl.random_inputs(B, H, N, N, d, dtype, seed=23)
+    scale = 1 / math.sqrt(d)
+    o_bits, lse = run(torch_mod, mha, qb, kb, vb, dtype, True, scale)
+    assert np.array_equal(o_bits[:, 0], vb[:, 0])  # bitwise
+    q, k = wl.bits_to_f64(qb, dtype), wl.bits_to_f64(kb, dtype)
+    want = np.float32(scale) * np.einsum("bhc,bhc->bh", q[:, 0], k[:, 0])
+    assert np.abs(lse[:, :, 0] - want).max() <= 1e-3
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "fp16")])
+def test_one_hot_dominance(torch_mod, mha, d, dtype):
+    B, H, Nq, Nk = 1, 1, 130, 200
+    jstar = 137
+    c = 320.0 if d == 64 else 512.0
+    scale = 1 / math.sqrt(d)
+    q = np.zeros((B, Nq, H, d))
+    q[..., 0] = c
+    k = np.zeros((B, Nk, H, d))
+    k[:, jstar, :, 0] = 1.0
+    vb = wl.random_inputs(B, H, Nk, Nk, d, dtype, seed=24)[2]
+    o_bits, lse = run(torch_mod, mha, _bits(q, dtype), _bits(k, dtype), vb, dtype, False, scale)
+    O = wl.bits_to_f64(o_bits, dtype)
+    v = wl.bits_to_f64(vb, dtype)
+    assert np.array_equal(O, np.broadcast_to(v[:, jstar:jstar + 1], O.shape))
+    t = c * np.float32(scale)
+    assert np.abs(lse - (t + math.log1p((Nk - 1) * math.exp(-t)))).max() <= 1e-3
+
+
+# -------------------------------------------------------- structural checks
+def test_deterministic(torch_mod, mha):
+    w = wl.WORKLOADS["encoder_self"]
+    qb, kb, vb = wl.make_inputs(w)
+    a = run(torch_mod, mha, qb, kb, vb, w.dtype, w.causal, w.scale)
+    b = run(torch_mod, mha, qb, kb, vb, w.dtype, w.causal, w.scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_head_and_batch_isolation(torch_mod, mha):
+    B, H, N, d, dtype = 2, 4, 200, 128, "bf16"
+    qb, kb, vb = wl.random_inputs(B, H, N, N, d, dtype, seed=25)
+    o1, l1 = run(torch_mod, mha, qb, kb, vb, dtype, True, 0.09)
+    q2, k2, v2 = qb.copy(), kb.copy(), vb.copy()
+    q2[:, :, 1:] ^= 0x0101   # perturb every other head
+    k2[1] ^= 0x0011          # and the other batch entry
+    v2[:, :, 2] ^= 0x0003
+    o2, l2 = run(torch_mod, mha, q2, k2, v2, dtype, True, 0.09)
+    assert np.array_equal(o1[0, :, 0], o2[0, :, 0])
+    assert np.array_equal(l1[0, 0], l2[0, 0])
+
+
+def test_affine_in_v(torch_mod, mha):
+    B, H, N, d, dtype = 1, 2, 190, 64, "fp16"
+    qb, kb, vb = wl.random_inputs(B, H, N, N, d, dtype, seed=26)
+    v = wl.bits_to_f64(vb, dtype)
+    o1, _ = run(torch_mod, mha, qb, kb, vb, dtype, False, 0.125)
+    o2, _ = run(torch_mod, mha, qb, kb, _bits(2 * v + 1, dtype), dtype, False, 0.125)
+    O1, O2 = wl.bits_to_f64(o1, dtype), wl.bits_to_f64(o2, dtype)
+    assert np.abs(O2 - (2 * O1 + 1)).max() <= 1e-2
+
+
+def test_causal_prefix_rows(torch_mod, mha):
+    """Causal row i equals the non-causal result over keys 0..i."""
+    B, H, N, d, dtype = 1, 1, 300, 128, "bf16"
+    qb, kb, vb = wl.random_inputs(B, H, N, N, d, dtype, seed=27)
+    o_c, l_c = run(torch_mod, mha, qb, kb, vb, dtype, True, 0.088)
+    for i in (0, 63, 64, 127, 128, 255, 299):
+        o_i, l_i = run(torch_mod, mha, qb[:, i:i + 1], kb[:, :i + 1], vb[:, :i + 1], dtype, False, 0.088)
+        Oc = wl.bits_to_f64(o_c[:, i], dtype)
+        Oi = wl.bits_to_f64(o_i[:, 0], dtype)
+        assert np.abs(Oc - Oi).max() <= 1e-2
+        assert abs(l_c[0, 0, i] - l_i[0, 0, 0]) <= 1e-4
+
+
+def test_runs_on_a_side_stream(torch_mod, mha):
+    torch = torch_mod
+    w = wl.WORKLOADS["tiny"]
+    qb, kb, vb = wl.make_inputs(w)
+    q, k, v = (to_dev(torch, x, w.dtype) for x in (qb, kb, vb))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = mha.attention(q, k, v, causal=False, scale=w.scale)
+    s.synchronize()
+    O_ref, L_ref = oracle.attention_fwd(*(wl.bits_to_f64(x, w.dtype) for x in (qb, kb, vb)),
+                                        False, w.scale)
+    assert_parity(compare(to_bits(o), lse.cpu().numpy(), O_ref, L_ref, w.dtype), "side stream")
+
+
+def test_error_paths_raise(torch_mod, mha):
+    torch = torch_mod
+    q = torch.zeros((1, 8, 1, 96), dtype=torch.float16, device="cuda")
+    with pytest.raises(mha.MhaError) as e:
+        mha.attention(q, q.clone(), q.clone())
+    assert e.value.status == mha.MHA_ERR_UNSUPPORTED
+    q = torch.zeros((1, 8, 1, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(mha.MhaError) as e:
+        mha.attention(q, q.clone(), q.clone(), scale=-1.0)
+    assert e.value.status == mha.MHA_ERR_INVALID_ARG
