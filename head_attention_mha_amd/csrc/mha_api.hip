@@ -127,6 +127,7 @@ mha_status_t mha_fwd(const void* q, const void* k, const void* v, void* o, float
   p.Nk = Nk;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.defer_raw = mha::kDeferLog2 / p.scale_log2;
   p.n_qtiles = (Nq + mha::kBQ - 1) / mha::kBQ;
   p.n_blocks = B * H * p.n_qtiles;
 

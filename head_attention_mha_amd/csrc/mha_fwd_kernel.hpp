@@ -8,7 +8,7 @@
 //   2. masks scores only on tiles that cross the causal diagonal or the end
 //      of the keys; tiles wholly past the causal frontier are never loaded;
 //   3. online softmax: running row max m and row sum l, O rescaled by
-//      alpha = exp(scale*(m_old - m_new));
+//      alpha = exp(scale*(m_old - m_new)) when the max has grown;
 //   4. converts P to bf16/f16 in registers and accumulates O^T += V^T . P^T
 //      on MFMA.
 // After the last tile O is divided by l, rounded to the I/O type and written
@@ -35,11 +35,19 @@
 //   consecutive keys per 16-key step -- exactly the B-operand fragment of the
 //   P.V product, so P needs no cross-lane layout change ("SparkAttention"
 //   step 3 becomes a register-local conversion).
-// * V is transposed on its way into LDS: each thread loads two keys' 8-wide
-//   rows and writes 32-bit words holding (V[2k][d], V[2k+1][d]); the V^T
-//   operand is then one 16-byte LDS read per MFMA.
-// * LDS tiles are XOR-swizzled in 16-byte units so the stores of the global
-//   rows and the MFMA operand reads are free of bank conflicts.
+// * K and V tiles are copied global -> LDS by buffer loads that write LDS
+//   directly (no staging registers); rows past the end of the keys read as
+//   zero through the buffer's range check, so the tail needs no branches.
+//   The copy of tile j+1 is in flight while tile j is computed.
+// * V stays row-major in LDS; the V^T operand of the P.V product comes from
+//   gfx950 LDS transpose reads (ds_read_b64_tr_b16), two per MFMA.
+// * LDS tiles are XOR-swizzled in 16-byte units so the MFMA operand reads
+//   are free of bank conflicts.
+// * The O rescale is deferred while a row's max stays within 2^8 (exp2
+//   domain) of the max O and l were last scaled to; O/l and LSE are the same
+//   in exact arithmetic, and the rescale then runs only when the max jumps.
+// * At most 256 registers per lane, so two waves share each SIMD and one
+//   wave's softmax overlaps the other's MFMAs.
 // * The 1-D grid is remapped so that consecutive work items of one head land
 //   on the same XCD (workgroups are dispatched round-robin over the 8 XCDs),
 //   keeping a head's K/V in that XCD's L2; causal query tiles run heaviest
@@ -101,6 +109,7 @@ struct Params {
   int B, H, Nq, Nk;
   float scale;       // softmax scale (> 0)
   float scale_log2;  // scale * log2(e): exp(scale*x) = exp2(scale_log2*x)
+  float defer_raw;   // rescale threshold in raw-score units: 8 / scale_log2
   int n_qtiles;      // ceil(Nq / BQ)
   int n_blocks;      // B * H * n_qtiles
 };
@@ -109,36 +118,68 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBQ = 32 * kWaves;  // query rows per workgroup
 constexpr int kBK = 64;           // keys per tile
+// The O rescale is deferred while a row's running max stays within 2^8 (in
+// the exp2 domain) of the reference max the accumulators were scaled to.
+constexpr float kDeferLog2 = 8.0f;
 
 // Row index of the K operand fed to MFMA row m: bits 2 and 3 of m swapped.
 __device__ __forceinline__ int k_row_order(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-// 16-byte-chunk swizzle of a K row in LDS (keeps 8 lanes of an operand read
-// on distinct banks for the row order above).
+// 16-byte-chunk swizzle of a K row in LDS: the 8 lanes of an operand read
+// (rows k_row_order(0..7)) land on 8 distinct chunk columns.
 __device__ __forceinline__ int k_swz(int key) { return (key & 3) | ((key >> 1) & 4); }
-// 16-byte-group swizzle of a V^T row (row = head-dim index) in LDS.
-__device__ __forceinline__ int vt_swz(int d) { return (d + (d >> 3)) & 7; }
+// 16-byte-chunk swizzle of a V row in LDS: the 4 rows x 32 bytes that 16
+// lanes of a transpose read touch land on 8 distinct chunk columns.
+__device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// gfx950 LDS transpose read of 4 x 16-bit values. Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte rows addressed by
+// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// One wave copies 1 KiB global -> LDS: lane l's 16 bytes at `voffset` land at
+// lds_dst + 16*l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)((lds_u8*)lds_dst),
+                                           16, voffset, 0, 0, 0);
+}
+
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mha_fwd_kernel(Params p) {
   using O_ = Ops<T>;
   constexpr int BK = kBK;
-  constexpr int KB = BK / 32;       // 32-key blocks per tile (S^T row blocks)
-  constexpr int DK = D / 16;        // k-steps of Q.K^T over the head dim
-  constexpr int DB = D / 32;        // 32-row blocks of O^T
-  constexpr int PK = BK / 16;       // k-steps of P.V over the keys
-  constexpr int CH = D / 8;         // 16-byte chunks per K/V row
-  constexpr int KU = BK * CH / kThreads;         // K chunks per thread per tile
-  constexpr int VW = BK / 2;                     // 32-bit words per V^T row
-  constexpr int VU = (BK / 2) * CH / kThreads;   // (key pair, chunk) units per thread
-  static_assert(KU >= 1 && VU >= 1, "tile too small for the workgroup");
+  constexpr int KB = BK / 32;            // 32-key blocks per tile (S^T row blocks)
+  constexpr int DK = D / 16;             // k-steps of Q.K^T over the head dim
+  constexpr int DB = D / 32;             // 32-row blocks of O^T
+  constexpr int PK = BK / 16;            // k-steps of P.V over the keys
+  constexpr int CH = D / 8;              // 16-byte chunks per K/V row
+  constexpr int ROWB = D * 2;            // bytes per K/V row in LDS
+  constexpr int TILEB = BK * ROWB;       // bytes per K or V tile
+  constexpr int RPI = 1024 / ROWB;       // rows per 1 KiB wave copy
+  constexpr int NCPW = TILEB / 1024 / kWaves;  // 1 KiB copies per wave per tensor
+  static_assert(NCPW >= 1, "tile too small for the workgroup");
 
-  __shared__ __attribute__((aligned(16))) u32x4 lds_k[2][BK * CH];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_vt[2][D * VW];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[TILEB];
 
   // ---- work item: (batch, head, query tile) --------------------------------
   const int lin = blockIdx.x;
@@ -156,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   const uint16_t* __restrict__ Kb = p.k + ((size_t)b * p.Nk * p.H + h) * D;
   const uint16_t* __restrict__ Vb = p.v + ((size_t)b * p.Nk * p.H + h) * D;
   uint16_t* __restrict__ Ob = p.o + ((size_t)b * p.Nq * p.H + h) * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -184,68 +226,28 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     n_kt = min(n_ktiles_all, (qmax + BK - 1) / BK);
   }
 
-  // ---- global -> register prefetch, register -> LDS store ------------------
-  u32x4 kreg[KU];
-  u32x4 vreg[VU][2];
+  // Per-lane source offsets of this wave's 1 KiB copies (same for every tile).
+  uint32_t k_off[NCPW], v_off[NCPW];
+#pragma unroll
+  for (int it = 0; it < NCPW; ++it) {
+    const int row = (it * kWaves + wave) * RPI + lane / CH;
+    const int pc = lane % CH;  // physical chunk in LDS
+    k_off[it] = row * row_bytes + 16 * (pc ^ k_swz(row));
+    v_off[it] = row * row_bytes + 16 * (pc ^ v_swz(row));
+  }
 
-  // V unit mapping: one wave instruction covers 8 chunks x (64/8) key pairs
-  // when CH == 8, or 16 chunks x 4 key pairs when CH == 16, so every key row
-  // is read as whole 128/256-byte segments.
-  auto v_unit = [&](int it, int& kp, int& dc) {
-    if constexpr (CH == 16) {
-      dc = (lane & 7) | ((lane >> 5) << 3);
-      kp = (it * kWaves + wave) * 4 + ((lane >> 3) & 3);
-    } else {
-      dc = lane & 7;
-      kp = (it * kWaves + wave) * 8 + (lane >> 3);
-    }
-  };
-
-  auto load_tile = [&](int j) {
+  // Issue the asynchronous global -> LDS copies of key tile j.
+  auto issue = [&](int j, uint8_t* lk, uint8_t* lv) {
     const int kbase = j * BK;
+    const int nvalid = min(BK, p.Nk - kbase);
+    const uint32_t bytes = (uint32_t)(nvalid - 1) * row_bytes + ROWB;
+    const auto rk = make_rsrc(Kb + (size_t)kbase * rs, bytes);
+    const auto rv = make_rsrc(Vb + (size_t)kbase * rs, bytes);
 #pragma unroll
-    for (int it = 0; it < KU; ++it) {
-      const int u = it * kThreads + tid;
-      const int key = u / CH, c = u % CH;
-      const int kk = kbase + key;
-      if (kk < p.Nk)
-        kreg[it] = *reinterpret_cast<const u32x4*>(Kb + (size_t)kk * rs + c * 8);
-      else
-        kreg[it] = u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int it = 0; it < VU; ++it) {
-      int kp, dc;
-      v_unit(it, kp, dc);
-      const int k0 = kbase + 2 * kp;
-      vreg[it][0] = (k0 < p.Nk) ? *reinterpret_cast<const u32x4*>(Vb + (size_t)k0 * rs + dc * 8)
-                                : u32x4{0, 0, 0, 0};
-      vreg[it][1] = (k0 + 1 < p.Nk)
-                        ? *reinterpret_cast<const u32x4*>(Vb + (size_t)(k0 + 1) * rs + dc * 8)
-                        : u32x4{0, 0, 0, 0};
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < KU; ++it) {
-      const int u = it * kThreads + tid;
-      const int key = u / CH, c = u % CH;
-      lds_k[buf][key * CH + (c ^ k_swz(key))] = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VU; ++it) {
-      int kp, dc;
-      v_unit(it, kp, dc);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t a = vreg[it][0][i >> 1];
-        const uint32_t bb = vreg[it][1][i >> 1];
-        const uint32_t word = (i & 1) ? ((a >> 16) | (bb & 0xffff0000u))
-                                      : ((a & 0xffffu) | (bb << 16));
-        const int d = dc * 8 + i;
-        lds_vt[buf][d * VW + (kp ^ (4 * vt_swz(d)))] = word;
-      }
+    for (int it = 0; it < NCPW; ++it) {
+      const int c = it * kWaves + wave;
+      dma16(rk, lk + c * 1024, k_off[it]);
+      dma16(rv, lv + c * 1024, v_off[it]);
     }
   };
 
@@ -255,98 +257,114 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_run = -INFINITY;  // running max of raw scores q.k
-  float l_run = 0.f;        // this lane's part of the running row sum
+  float m_run = -INFINITY;  // reference max (raw scores q.k) of o and l_run
+  float l_run = 0.f;        // this lane's part of the row sum
   const float c = p.scale_log2;
 
-  load_tile(0);
-  store_tile(0);
-
-  for (int j = 0; j < n_kt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_kt) load_tile(j + 1);
-    __syncthreads();
-
+  auto compute = [&](int j, const uint8_t* lk, const uint8_t* lv) {
     const int k0 = j * BK;
-    const bool active = !CAUSAL || k0 <= qw0 + 31;
-    if (active) {
-      // S^T = K . Q^T for 64 keys x 32 queries
-      f32x16 s[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const int key = kb * 32 + k_row_order(ln);
-        const u32x4* krow = &lds_k[buf][key * CH];
-        const int sw = k_swz(key);
-#pragma unroll
-        for (int i = 0; i < DK; ++i) s[kb] = O_::mfma(krow[(2 * i + hf) ^ sw], qf[i], s[kb]);
-      }
+    if (CAUSAL && k0 > qw0 + 31) return;  // tile wholly past this wave's rows
 
-      // mask only where the tile crosses the diagonal or the end of the keys
-      const bool need_mask = (k0 + BK > p.Nk) || (CAUSAL && k0 + BK - 1 > qw0);
-      if (need_mask) {
+    // S^T = K . Q^T for 64 keys x 32 queries
+    f32x16 s[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-            const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
-            s[kb][r] = vis ? s[kb][r] : -INFINITY;
-          }
-      }
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      const int key = kb * 32 + k_row_order(ln);
+      const uint8_t* krow = lk + key * ROWB;
+      const int sw = k_swz(key);
+#pragma unroll
+      for (int i = 0; i < DK; ++i)
+        s[kb] = O_::mfma(*reinterpret_cast<const u32x4*>(krow + 16 * ((2 * i + hf) ^ sw)), qf[i], s[kb]);
+    }
 
-      // online softmax
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2((m_run - m_new) * c);
-      const float mc = m_new * c;
-      float rsum = 0.f;
+    // mask only where the tile crosses the diagonal or the end of the keys
+    const bool need_mask = (k0 + BK > p.Nk) || (CAUSAL && k0 + BK - 1 > qw0);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
-          s[kb][r] = e;
-          rsum += e;
+          const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
+          const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
+    }
+
+    // online softmax; the rescale of O and l is deferred while the tile max
+    // stays within kDeferLog2 of the reference max
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + p.defer_raw)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2((m_run - m_new) * c);
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-
-      // P^T fragments: k-step ks covers keys 16*ks + 8*hf + 0..7
-      u32x4 pf[PK];
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
+    float rsum = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < PK; ++ks) {
-        const int kb = ks >> 1, r0 = 8 * (ks & 1);
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) pf[ks][t] = O_::pack(s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1]);
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
+        s[kb][r] = e;
+        rsum += e;
       }
+    l_run += rsum;
 
-      // O^T += V^T . P^T
+    // P^T fragments: k-step ks covers keys 16*ks + 8*hf + 0..7
+    u32x4 pf[PK];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = db * 32 + ln;
-        const uint32_t* vrow = &lds_vt[buf][d * VW];
-        const int sw = vt_swz(d);
+    for (int ks = 0; ks < PK; ++ks) {
+      const int kb = ks >> 1, r0 = 8 * (ks & 1);
 #pragma unroll
-        for (int ks = 0; ks < PK; ++ks) {
-          const int g = 2 * ks + hf;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + 4 * (g ^ sw));
-          o[db] = O_::mfma(a, pf[ks], o[db]);
-        }
-      }
+      for (int t = 0; t < 4; ++t) pf[ks][t] = O_::pack(s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1]);
     }
 
-    if (j + 1 < n_kt) store_tile(buf ^ 1);
+    // O^T += V^T . P^T; V^T fragments by transpose reads of row-major V
+    const int grp = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int dch = 4 * db + 2 * (grp & 1) + ((li & 3) >> 1);  // 16-byte chunk of d
+      const int dsub = 8 * (li & 1);                              // byte offset in the chunk
+#pragma unroll
+      for (int ks = 0; ks < PK; ++ks) {
+        u32x4 a;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int key = ks * 16 + 8 * (grp >> 1) + 4 * r + (li >> 2);
+          const u32x2 t = lds_read_tr16(lv + key * ROWB + 16 * (dch ^ v_swz(key)) + dsub);
+          a[2 * r] = t[0];
+          a[2 * r + 1] = t[1];
+        }
+        o[db] = O_::mfma(a, pf[ks], o[db]);
+      }
+    }
+  };
+
+  // ---- main loop: double-buffered, one barrier per key tile ----------------
+  issue(0, lds_k0, lds_v0);
+  for (int j = 0; j < n_kt; j += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile j landed
+    __syncthreads();
+    if (j + 1 < n_kt) issue(j + 1, lds_k1, lds_v1);
+    compute(j, lds_k0, lds_v0);
+    if (j + 1 < n_kt) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (j + 2 < n_kt) issue(j + 2, lds_k0, lds_v0);
+      compute(j + 1, lds_k1, lds_v1);
+    }
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale*m + ln(l) ------------------------
