@@ -57,6 +57,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mha {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -85,6 +87,11 @@ struct Ops<BF16> {
     f32x2 v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
+  // Row-sum update for two probabilities: in fp32 (bf16 keeps 8 significant
+  // bits, too few for the LSE bound on rows with few keys).
+  static __device__ __forceinline__ float sum2(uint32_t, float x, float y, float acc) {
+    return acc + x + y;
+  }
 };
 
 template <>
@@ -97,6 +104,12 @@ struct Ops<F16> {
   static __device__ __forceinline__ uint32_t pack(float x, float y) {
     f32x2 v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  // Row-sum update for two probabilities from their packed f16 values: one
+  // v_dot2 with (1, 1) (f16 keeps 11 significant bits).
+  static __device__ __forceinline__ float sum2(uint32_t packed, float, float, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
   }
 };
 
@@ -122,16 +135,29 @@ constexpr int kBK = 64;           // keys per tile
 // the exp2 domain) of the reference max the accumulators were scaled to.
 constexpr float kDeferLog2 = 8.0f;
 
-// Row index of the K operand fed to MFMA row m: bits 2 and 3 of m swapped.
+// Row index of the K operand fed to MFMA row m: bits 2 and 3 of m swapped
+// (an involution).
 __device__ __forceinline__ int k_row_order(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-// 16-byte-chunk swizzle of a K row in LDS: the 8 lanes of an operand read
-// (rows k_row_order(0..7)) land on 8 distinct chunk columns.
-__device__ __forceinline__ int k_swz(int key) { return (key & 3) | ((key >> 1) & 4); }
-// 16-byte-chunk swizzle of a V row in LDS: the 4 rows x 32 bytes that 16
-// lanes of a transpose read touch land on 8 distinct chunk columns.
-__device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3); }
+// 16-byte-chunk swizzles of the K and V rows in LDS. They are chosen so that
+// the lanes of one LDS pass hit distinct banks whether the LDS serves 8 lanes
+// x 16 bytes (b128) / 16 lanes x 8 bytes (b64) per 128-byte pass, or 16 x 16
+// / 32 x 8 per 256-byte pass.
+//  K, read as S^T A-operand rows: lane m (of 16) reads row k_row_order(m).
+template <int D>
+__device__ __forceinline__ int k_swz(int key) {
+  const int m = k_row_order(key & 15);
+  if constexpr (D == 128) return m;            // 16 chunks per 256-byte row
+  else return (m >> 1) ^ (4 * (m & 1));        // 8 chunks per 128-byte row
+}
+//  V, read by transpose reads: 16 lanes touch 4 consecutive rows x 32 bytes.
+template <int D>
+__device__ __forceinline__ int v_swz(int key) {
+  const int t = key & 3;
+  if constexpr (D == 128) return 4 * t + 2 * (t >> 1);
+  else return 2 * t;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -232,12 +258,12 @@ void mha_fwd_kernel(Params p) {
   for (int it = 0; it < NCPW; ++it) {
     const int row = (it * kWaves + wave) * RPI + lane / CH;
     const int pc = lane % CH;  // physical chunk in LDS
-    k_off[it] = row * row_bytes + 16 * (pc ^ k_swz(row));
-    v_off[it] = row * row_bytes + 16 * (pc ^ v_swz(row));
+    k_off[it] = row * row_bytes + 16 * (pc ^ k_swz<D>(row));
+    v_off[it] = row * row_bytes + 16 * (pc ^ v_swz<D>(row));
   }
 
   // Issue the asynchronous global -> LDS copies of key tile j.
-  auto issue = [&](int j, uint8_t* lk, uint8_t* lv) {
+  auto issue = [&](int j, uint8_t* lk, uint8_t* lv) __attribute__((always_inline)) {
     const int kbase = j * BK;
     const int nvalid = min(BK, p.Nk - kbase);
     const uint32_t bytes = (uint32_t)(nvalid - 1) * row_bytes + ROWB;
@@ -261,27 +287,43 @@ void mha_fwd_kernel(Params p) {
   float l_run = 0.f;        // this lane's part of the row sum
   const float c = p.scale_log2;
 
-  auto compute = [&](int j, const uint8_t* lk, const uint8_t* lv) {
+  // Key tiles [0, jm) need no element mask for any row of this workgroup;
+  // [jm, n_kt) may (the last, partial tile; the tiles crossing the causal
+  // diagonal of rows q0 .. q0+BQ-1).
+  int jm = (p.Nk % BK) ? p.Nk / BK : n_ktiles_all;
+  if (CAUSAL) jm = min(jm, (q0 + 1) / BK);
+  jm = min(jm, n_kt);
+
+  auto compute = [&](int j, const uint8_t* lk, const uint8_t* lv, bool masked)
+                     __attribute__((always_inline)) {
     const int k0 = j * BK;
     if (CAUSAL && k0 > qw0 + 31) return;  // tile wholly past this wave's rows
 
-    // S^T = K . Q^T for 64 keys x 32 queries
+    // S^T = K . Q^T for 64 keys x 32 queries: two independent accumulation
+    // chains (one per 32-key block), interleaved per k-step
     f32x16 s[KB];
+    const uint8_t* krow[KB];
+    int ksw[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
       const int key = kb * 32 + k_row_order(ln);
-      const uint8_t* krow = lk + key * ROWB;
-      const int sw = k_swz(key);
-#pragma unroll
-      for (int i = 0; i < DK; ++i)
-        s[kb] = O_::mfma(*reinterpret_cast<const u32x4*>(krow + 16 * ((2 * i + hf) ^ sw)), qf[i], s[kb]);
+      krow[kb] = lk + key * ROWB;
+      ksw[kb] = k_swz<D>(key);
     }
+#pragma unroll
+    for (int i = 0; i < DK; ++i)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        s[kb] = O_::mfma(*reinterpret_cast<const u32x4*>(krow[kb] + 16 * ((2 * i + hf) ^ ksw[kb])),
+                         qf[i], s[kb]);
 
-    // mask only where the tile crosses the diagonal or the end of the keys
-    const bool need_mask = (k0 + BK > p.Nk) || (CAUSAL && k0 + BK - 1 > qw0);
-    if (need_mask) {
+    // mask only where the tile crosses the diagonal or the end of the keys;
+    // the empty asm keeps the compiler from turning this rarely taken,
+    // wave-uniform branch into selects executed on every tile
+    if (masked) {
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -311,39 +353,39 @@ void mha_fwd_kernel(Params p) {
       m_run = m_new;
     }
     const float mc = m_run * c;
-    float rsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
-        s[kb][r] = e;
-        rsum += e;
-      }
-    l_run += rsum;
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
 
-    // P^T fragments: k-step ks covers keys 16*ks + 8*hf + 0..7
+    // P^T fragments: k-step ks covers keys 16*ks + 8*hf + 0..7.
     u32x4 pf[PK];
+    float rsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < PK; ++ks) {
       const int kb = ks >> 1, r0 = 8 * (ks & 1);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) pf[ks][t] = O_::pack(s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1]);
+      for (int t = 0; t < 4; ++t) {
+        pf[ks][t] = O_::pack(s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1]);
+        rsum = O_::sum2(pf[ks][t], s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1], rsum);
+      }
     }
+    l_run += rsum;
 
-    // O^T += V^T . P^T; V^T fragments by transpose reads of row-major V
+    // O^T += V^T . P^T; V^T fragments by transpose reads of row-major V. The
+    // DB accumulators are independent, so they are interleaved per k-step.
     const int grp = lane >> 4, li = lane & 15;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int dch = 4 * db + 2 * (grp & 1) + ((li & 3) >> 1);  // 16-byte chunk of d
-      const int dsub = 8 * (li & 1);                              // byte offset in the chunk
+    for (int ks = 0; ks < PK; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < PK; ++ks) {
+      for (int db = 0; db < DB; ++db) {
+        const int dch = 4 * db + 2 * (grp & 1) + ((li & 3) >> 1);  // 16-byte chunk of d
+        const int dsub = 8 * (li & 1);                              // byte offset in it
         u32x4 a;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int key = ks * 16 + 8 * (grp >> 1) + 4 * r + (li >> 2);
-          const u32x2 t = lds_read_tr16(lv + key * ROWB + 16 * (dch ^ v_swz(key)) + dsub);
+          const u32x2 t = lds_read_tr16(lv + key * ROWB + 16 * (dch ^ v_swz<D>(key)) + dsub);
           a[2 * r] = t[0];
           a[2 * r + 1] = t[1];
         }
@@ -353,18 +395,24 @@ void mha_fwd_kernel(Params p) {
   };
 
   // ---- main loop: double-buffered, one barrier per key tile ----------------
-  issue(0, lds_k0, lds_v0);
-  for (int j = 0; j < n_kt; j += 2) {
+  // step: wait for tile j in buffer `buf`, start the copy of tile j+1 into
+  // the other buffer (last read by tile j-1, which every wave has finished
+  // once past the barrier), then compute tile j.
+  auto step = [&](int j, auto buf) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile j landed
     __syncthreads();
-    if (j + 1 < n_kt) issue(j + 1, lds_k1, lds_v1);
-    compute(j, lds_k0, lds_v0);
-    if (j + 1 < n_kt) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      if (j + 2 < n_kt) issue(j + 2, lds_k0, lds_v0);
-      compute(j + 1, lds_k1, lds_v1);
+    if constexpr (decltype(buf)::value == 0) {
+      if (j + 1 < n_kt) issue(j + 1, lds_k1, lds_v1);
+      compute(j, lds_k0, lds_v0, j >= jm);
+    } else {
+      if (j + 1 < n_kt) issue(j + 1, lds_k0, lds_v0);
+      compute(j, lds_k1, lds_v1, j >= jm);
     }
+  };
+  issue(0, lds_k0, lds_v0);
+  for (int j = 0; j < n_kt; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < n_kt) step(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale*m + ln(l) ------------------------
