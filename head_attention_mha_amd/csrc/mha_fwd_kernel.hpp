@@ -1,8 +1,8 @@
 // Fused multi-head attention forward for gfx950 (CDNA4).
 //
-// One workgroup (4 wave64 waves) owns BQ = 128 query rows of one (batch, head)
-// and streams that head's keys and values through LDS in tiles of BK = 64
-// keys, double-buffered. Per key tile each wave, for its 32 query rows:
+// One workgroup (8 wave64 waves) owns BQ = 256 query rows of one (batch,
+// head), 32 per wave, and streams that head's keys and values through LDS in
+// tiles of BK = 64 keys. Per key tile each wave, for its 32 query rows:
 //
 //   1. S^T = K_tile . Q^T on MFMA 32x32x16 (bf16/f16 in, fp32 accumulate);
 //   2. masks scores only on tiles that cross the causal diagonal or the end
@@ -26,6 +26,11 @@
 // "StreamKL", Methodology sections 1-2.
 //
 // gfx950 choices (not from the pages):
+// * Ping-pong of two wave groups. Waves 0-3 and 4-7 each alternate a GEMM
+//   phase (P.V of the previous tile and S^T of the current tile, 32 MFMAs)
+//   and a softmax phase (VALU), the second group half a period behind the
+//   first, with workgroup barriers between phases: every SIMD holds one wave
+//   of each group, so one issues MFMAs while the other runs its softmax.
 // * S is computed transposed (keys are MFMA rows, queries are columns), so
 //   each lane owns one query: the row max needs one exchange between lanes
 //   l and l^32, the row sum needs none until the end, and alpha is a
@@ -38,16 +43,15 @@
 // * K and V tiles are copied global -> LDS by buffer loads that write LDS
 //   directly (no staging registers); rows past the end of the keys read as
 //   zero through the buffer's range check, so the tail needs no branches.
-//   The copy of tile j+1 is in flight while tile j is computed.
+//   Copies run two phases ahead of their first use.
 // * V stays row-major in LDS; the V^T operand of the P.V product comes from
 //   gfx950 LDS transpose reads (ds_read_b64_tr_b16), two per MFMA.
 // * LDS tiles are XOR-swizzled in 16-byte units so the MFMA operand reads
-//   are free of bank conflicts.
+//   are free of bank conflicts; the GEMM phase reads each operand four MFMAs
+//   ahead of its use.
 // * The O rescale is deferred while a row's max stays within 2^8 (exp2
 //   domain) of the max O and l were last scaled to; O/l and LSE are the same
 //   in exact arithmetic, and the rescale then runs only when the max jumps.
-// * At most 256 registers per lane, so two waves share each SIMD and one
-//   wave's softmax overlaps the other's MFMAs.
 // * The 1-D grid is remapped so that consecutive work items of one head land
 //   on the same XCD (workgroups are dispatched round-robin over the 8 XCDs),
 //   keeping a head's K/V in that XCD's L2; causal query tiles run heaviest
@@ -127,9 +131,9 @@ struct Params {
   int n_blocks;      // B * H * n_qtiles
 };
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;          // two groups of four: one wave of each per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBQ = 32 * kWaves;  // query rows per workgroup
+constexpr int kBQ = 32 * kWaves;  // query rows per workgroup (32 per wave)
 constexpr int kBK = 64;           // keys per tile
 // The O rescale is deferred while a row's running max stays within 2^8 (in
 // the exp2 domain) of the reference max the accumulators were scaled to.
@@ -186,9 +190,31 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
                                            16, voffset, 0, 0, 0);
 }
 
+// Scheduling pins for the GEMM phase: the reads of the first AHEAD operands,
+// then for every MFMA n one MFMA followed by the reads of operand n+AHEAD
+// (two 8-byte transpose reads for a V^T operand, one 16-byte read for a K
+// operand).
+template <int N, int NPV, int NS, int AHEAD>
+struct PinInterleave {
+  static constexpr int reads_of(int n) { return n < NPV ? 2 : 1; }
+  static constexpr int preload() {
+    int r = 0;
+    for (int n = 0; n < AHEAD; ++n) r += reads_of(n);
+    return r;
+  }
+  static __device__ __forceinline__ void apply() {
+    if constexpr (N == 0) __builtin_amdgcn_sched_group_barrier(0x100, preload(), 0);
+    if constexpr (N < NPV + NS) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (N + AHEAD < NPV + NS)
+        __builtin_amdgcn_sched_group_barrier(0x100, reads_of(N + AHEAD), 0);
+      PinInterleave<N + 1, NPV, NS, AHEAD>::apply();
+    }
+  }
+};
+
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mha_fwd_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   using O_ = Ops<T>;
   constexpr int BK = kBK;
   constexpr int KB = BK / 32;            // 32-key blocks per tile (S^T row blocks)
@@ -226,7 +252,8 @@ void mha_fwd_kernel(Params p) {
   const uint32_t row_bytes = (uint32_t)(rs * 2);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;       // 0: group A, 1: group B (half a period later)
   const int lane = tid & 63;
   const int ln = lane & 31;
   const int hf = lane >> 5;
@@ -251,8 +278,15 @@ void mha_fwd_kernel(Params p) {
     const int qmax = min(p.Nq, q0 + kBQ);  // one past the last visible query
     n_kt = min(n_ktiles_all, (qmax + BK - 1) / BK);
   }
+  // Tiles [0, jm) need no element mask for this wave's rows; later ones may
+  // (the last, partial tile; tiles reaching past row qw0 when causal).
+  int jm = (p.Nk % BK) ? p.Nk / BK : n_ktiles_all;
+  if (CAUSAL) jm = min(jm, (qw0 + 1) / BK);
+  // Tiles from j_end on lie wholly past this wave's rows (causal) or past
+  // the keys: this wave skips them.
+  const int j_end = CAUSAL ? min(n_kt, qw0 / BK + 1) : n_kt;
 
-  // Per-lane source offsets of this wave's 1 KiB copies (same for every tile).
+  // ---- asynchronous global -> LDS copies ------------------------------------
   uint32_t k_off[NCPW], v_off[NCPW];
 #pragma unroll
   for (int it = 0; it < NCPW; ++it) {
@@ -261,21 +295,46 @@ void mha_fwd_kernel(Params p) {
     k_off[it] = row * row_bytes + 16 * (pc ^ k_swz<D>(row));
     v_off[it] = row * row_bytes + 16 * (pc ^ v_swz<D>(row));
   }
-
-  // Issue the asynchronous global -> LDS copies of key tile j.
-  auto issue = [&](int j, uint8_t* lk, uint8_t* lv) __attribute__((always_inline)) {
+  auto rsrc_for = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
     const int kbase = j * BK;
     const int nvalid = min(BK, p.Nk - kbase);
-    const uint32_t bytes = (uint32_t)(nvalid - 1) * row_bytes + ROWB;
-    const auto rk = make_rsrc(Kb + (size_t)kbase * rs, bytes);
-    const auto rv = make_rsrc(Vb + (size_t)kbase * rs, bytes);
-#pragma unroll
-    for (int it = 0; it < NCPW; ++it) {
-      const int c = it * kWaves + wave;
-      dma16(rk, lk + c * 1024, k_off[it]);
-      dma16(rv, lv + c * 1024, v_off[it]);
-    }
+    return make_rsrc(base + (size_t)kbase * rs, (uint32_t)(nvalid - 1) * row_bytes + ROWB);
   };
+  auto issue_k = [&](int j, uint8_t* lk) __attribute__((always_inline)) {
+    const auto r = rsrc_for(Kb, j);
+#pragma unroll
+    for (int it = 0; it < NCPW; ++it) dma16(r, lk + (it * kWaves + wave) * 1024, k_off[it]);
+  };
+  auto issue_v = [&](int j, uint8_t* lv) __attribute__((always_inline)) {
+    const auto r = rsrc_for(Vb, j);
+#pragma unroll
+    for (int it = 0; it < NCPW; ++it) dma16(r, lv + (it * kWaves + wave) * 1024, v_off[it]);
+  };
+
+  // ---- per-lane LDS read offsets (fixed for the whole kernel) ---------------
+  // K operand: MFMA row ln reads key kb*32 + k_row_order(ln); its chunk
+  // swizzle depends only on the key's low 4 bits, i.e. only on ln, so one
+  // offset per k-step serves both 32-key blocks (+32 rows) and both buffers.
+  uint32_t koff[DK];
+  {
+    const int key = k_row_order(ln);
+    const int sw = k_swz<D>(key);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) koff[i] = key * ROWB + 16 * ((2 * i + hf) ^ sw);
+  }
+  // V transpose read: lane (g16, li) of a 16-key step reads key
+  // 8*(g16>>1) + 4r + (li>>2), 8-byte piece (li&1) of 16-byte chunk
+  // 4*db + 2*(g16&1) + ((li&3)>>1). The V swizzle depends only on li>>2, so
+  // one offset per 32-row block db serves every key step (+16 rows) and r.
+  uint32_t voff[DB];
+  {
+    const int g16 = lane >> 4, li = lane & 15;
+    const int key = 8 * (g16 >> 1) + (li >> 2);
+    const int sw = v_swz<D>(key);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      voff[db] = key * ROWB + 16 * ((4 * db + 2 * (g16 & 1) + ((li & 3) >> 1)) ^ sw) + 8 * (li & 1);
+  }
 
   // ---- running state -------------------------------------------------------
   f32x16 o[DB];
@@ -283,46 +342,88 @@ void mha_fwd_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  f32x16 s[KB];             // S^T of the tile between its GEMM and softmax phases
+  u32x4 pf[PK];             // packed P^T between the softmax and the next GEMM phase
+#pragma unroll
+  for (int ks = 0; ks < PK; ++ks) pf[ks] = u32x4{0, 0, 0, 0};
   float m_run = -INFINITY;  // reference max (raw scores q.k) of o and l_run
   float l_run = 0.f;        // this lane's part of the row sum
   const float c = p.scale_log2;
 
-  // Key tiles [0, jm) need no element mask for any row of this workgroup;
-  // [jm, n_kt) may (the last, partial tile; the tiles crossing the causal
-  // diagonal of rows q0 .. q0+BQ-1).
-  int jm = (p.Nk % BK) ? p.Nk / BK : n_ktiles_all;
-  if (CAUSAL) jm = min(jm, (q0 + 1) / BK);
-  jm = min(jm, n_kt);
-
-  auto compute = [&](int j, const uint8_t* lk, const uint8_t* lv, bool masked)
-                     __attribute__((always_inline)) {
-    const int k0 = j * BK;
-    if (CAUSAL && k0 > qw0 + 31) return;  // tile wholly past this wave's rows
-
-    // S^T = K . Q^T for 64 keys x 32 queries: two independent accumulation
-    // chains (one per 32-key block), interleaved per k-step
-    f32x16 s[KB];
-    const uint8_t* krow[KB];
-    int ksw[KB];
+  // GEMM phase of tile j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T.
+  // The 16 + 16 MFMAs are one straight-line sequence; the LDS operand of
+  // MFMA n+kAhead is read while MFMA n issues, so LDS latency stays hidden
+  // behind MFMA work. The per-lane offsets pass through an empty asm so the
+  // compiler forms each address here (buffer base in the instruction's
+  // immediate offset) instead of hoisting one register per (buffer, step).
+  constexpr int NPV = PK * DB;  // P.V MFMAs per tile
+  constexpr int NS = DK * KB;   // S^T MFMAs per tile
+  constexpr int kAhead = 4;
+  // One code path for every GEMM phase (distinct paths would each keep O in
+  // their own registers and copy it across on every tile): for j = 0 the
+  // P.V MFMAs multiply P = 0 with a zero-filled V buffer, and for j = j_end
+  // the S^T MFMAs produce a tile nobody reads.
+  auto gemm = [&](int j, const uint8_t* lk, const uint8_t* lv) __attribute__((always_inline)) {
+    if (j > j_end) return;  // wave-uniform: past this wave's rows
+    uint32_t vo[DB], ko[DK];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int key = kb * 32 + k_row_order(ln);
-      krow[kb] = lk + key * ROWB;
-      ksw[kb] = k_swz<D>(key);
+    for (int db = 0; db < DB; ++db) {
+      vo[db] = voff[db];
+      asm volatile("" : "+v"(vo[db]));
     }
 #pragma unroll
-    for (int i = 0; i < DK; ++i)
+    for (int i = 0; i < DK; ++i) {
+      ko[i] = koff[i];
+      asm volatile("" : "+v"(ko[i]));
+    }
+    // operand of MFMA n: n < NPV -> V^T fragment (ks, db) = (n / DB, n % DB);
+    // else K fragment (i, kb) = ((n - NPV) / KB, (n - NPV) % KB)
+    auto load_op = [&](int n) __attribute__((always_inline)) -> u32x4 {
+      u32x4 a;
+      if (n < NPV) {
+        const int ks = n / DB, db = n % DB;
+        const u32x2 t0 = lds_read_tr16(lv + vo[db] + (ks * 16) * ROWB);
+        const u32x2 t1 = lds_read_tr16(lv + vo[db] + (ks * 16 + 4) * ROWB);
+        a[0] = t0[0];
+        a[1] = t0[1];
+        a[2] = t1[0];
+        a[3] = t1[1];
+      } else {
+        const int m = n - NPV, i = m / KB, kb = m % KB;
+        a = *reinterpret_cast<const u32x4*>(lk + ko[i] + kb * 32 * ROWB);
+      }
+      return a;
+    };
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        s[kb] = O_::mfma(*reinterpret_cast<const u32x4*>(krow[kb] + 16 * ((2 * i + hf) ^ ksw[kb])),
-                         qf[i], s[kb]);
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    u32x4 buf[kAhead];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) buf[n] = load_op(n);
+#pragma unroll
+    for (int n = 0; n < NPV + NS; ++n) {
+      const u32x4 a = buf[n % kAhead];
+      if (n + kAhead < NPV + NS) buf[n % kAhead] = load_op(n + kAhead);
+      if (n < NPV) {
+        const int ks = n / DB, db = n % DB;
+        o[db] = O_::mfma(a, pf[ks], o[db]);
+      } else {
+        const int m = n - NPV, i = m / KB, kb = m % KB;
+        s[kb] = O_::mfma(a, qf[i], s[kb]);
+      }
+    }
+    // pin the order: the preloads, then per MFMA the reads kAhead ahead
+    PinInterleave<0, NPV, NS, kAhead>::apply();
+  };
 
-    // mask only where the tile crosses the diagonal or the end of the keys;
-    // the empty asm keeps the compiler from turning this rarely taken,
-    // wave-uniform branch into selects executed on every tile
-    if (masked) {
+  // Softmax phase of tile j: mask, running max, exp, row sum, P^T fragments.
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    if (j >= j_end) return;
+    const int k0 = j * BK;
+    if (j >= jm) {
+      // the empty asm keeps the compiler from turning this rarely taken,
+      // wave-uniform branch into selects executed on every tile
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -333,15 +434,14 @@ void mha_fwd_kernel(Params p) {
           s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
     }
-
-    // online softmax; the rescale of O and l is deferred while the tile max
-    // stays within kDeferLog2 of the reference max
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // the O and l rescale is deferred while the max stays within
+    // kDeferLog2 of the reference max
     if (__any(mx > m_run + p.defer_raw)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2((m_run - m_new) * c);
@@ -357,9 +457,7 @@ void mha_fwd_kernel(Params p) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
-
-    // P^T fragments: k-step ks covers keys 16*ks + 8*hf + 0..7.
-    u32x4 pf[PK];
+    // P^T fragments: k-step ks covers keys 16*ks + 8*hf + 0..7
     float rsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < PK; ++ks) {
@@ -371,48 +469,102 @@ void mha_fwd_kernel(Params p) {
       }
     }
     l_run += rsum;
-
-    // O^T += V^T . P^T; V^T fragments by transpose reads of row-major V. The
-    // DB accumulators are independent, so they are interleaved per k-step.
-    const int grp = lane >> 4, li = lane & 15;
-#pragma unroll
-    for (int ks = 0; ks < PK; ++ks) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int dch = 4 * db + 2 * (grp & 1) + ((li & 3) >> 1);  // 16-byte chunk of d
-        const int dsub = 8 * (li & 1);                              // byte offset in it
-        u32x4 a;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int key = ks * 16 + 8 * (grp >> 1) + 4 * r + (li >> 2);
-          const u32x2 t = lds_read_tr16(lv + key * ROWB + 16 * (dch ^ v_swz<D>(key)) + dsub);
-          a[2 * r] = t[0];
-          a[2 * r + 1] = t[1];
-        }
-        o[db] = O_::mfma(a, pf[ks], o[db]);
-      }
-    }
   };
 
-  // ---- main loop: double-buffered, one barrier per key tile ----------------
-  // step: wait for tile j in buffer `buf`, start the copy of tile j+1 into
-  // the other buffer (last read by tile j-1, which every wave has finished
-  // once past the barrier), then compute tile j.
-  auto step = [&](int j, auto buf) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile j landed
-    __syncthreads();
+  // ---- phase schedule ------------------------------------------------------
+  // The workgroup steps through phases separated by barriers #0, #1, ...;
+  // phase p runs between barriers #p and #p+1. Group A (grp 0) runs the
+  // GEMM phase of tile j in phase 2j and its softmax phase in phase 2j+1;
+  // group B runs the same sequence one phase later, so on every SIMD one
+  // wave issues MFMAs while the other runs its softmax. Each group has its
+  // own straight-line loop; the k-th barrier of every wave pairs up.
+  // K_j is read in phases 2j and 2j+1, V_j in phases 2j+2 and 2j+3. At the
+  // start of each even phase 2m every wave starts its share of the copies of
+  // K_{m+1} and V_m, into the buffers that held K_{m-1} and V_{m-2} (last
+  // read in phase 2m-1), and waits for them just before barrier #2m+2.
+  auto barrier = [&]() __attribute__((always_inline)) { __syncthreads(); };
+  auto wait_copies = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
+  // Copies of K_{m+1} and V_m; BUF = m & 1 (compile time).
+  auto issue_pair = [&](int m, auto buf) __attribute__((always_inline)) {
     if constexpr (decltype(buf)::value == 0) {
-      if (j + 1 < n_kt) issue(j + 1, lds_k1, lds_v1);
-      compute(j, lds_k0, lds_v0, j >= jm);
+      if (m + 1 < n_kt) issue_k(m + 1, lds_k1);
+      if (m < n_kt) issue_v(m, lds_v0);
     } else {
-      if (j + 1 < n_kt) issue(j + 1, lds_k0, lds_v0);
-      compute(j, lds_k1, lds_v1, j >= jm);
+      if (m + 1 < n_kt) issue_k(m + 1, lds_k0);
+      if (m < n_kt) issue_v(m, lds_v1);
     }
   };
-  issue(0, lds_k0, lds_v0);
-  for (int j = 0; j < n_kt; j += 2) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < n_kt) step(j + 1, std::integral_constant<int, 1>{});
+  // GEMM phase of tile j with BUF = j & 1: K_j in K buffer BUF, V_{j-1} in
+  // V buffer BUF ^ 1.
+  auto gemm_phase = [&](int j, auto buf) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(2);
+    if constexpr (decltype(buf)::value == 0)
+      gemm(j, lds_k0, lds_v1);
+    else
+      gemm(j, lds_k1, lds_v0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // the first GEMM phase multiplies P = 0 with V buffer 1: make it finite
+  for (int i = tid; i < TILEB / 16; i += kThreads)
+    reinterpret_cast<u32x4*>(lds_v1)[i] = u32x4{0, 0, 0, 0};
+  issue_k(0, lds_k0);
+  wait_copies();
+  barrier();  // #0
+  if (grp == 0) {
+    // group A: phase 2j = GEMM(j), phase 2j+1 = softmax(j)
+    auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
+      issue_pair(j, buf);       // start of phase 2j
+      gemm_phase(j, buf);
+      barrier();                // #2j+1
+      softmax(j);
+      wait_copies();
+      barrier();                // #2j+2
+    };
+    int j = 0;
+    for (; j + 1 < n_kt; j += 2) {
+      tile(j, I0{});
+      tile(j + 1, I1{});
+    }
+    if (j < n_kt) {
+      tile(j, I0{});
+      ++j;
+    }
+    // phase 2n: P.V of the last tile, then barrier #2n+1 to match group B
+    if (j & 1) gemm_phase(j, I1{});
+    else gemm_phase(j, I0{});
+    barrier();
+  } else {
+    // group B: phase 2j+1 = GEMM(j), phase 2j+2 = softmax(j)
+    issue_pair(0, I0{});        // start of phase 0
+    barrier();                  // #1
+    auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
+      gemm_phase(j, buf);
+      wait_copies();
+      barrier();                // #2j+2
+      if constexpr (decltype(buf)::value == 0)
+        issue_pair(j + 1, I1{});  // start of phase 2j+2
+      else
+        issue_pair(j + 1, I0{});
+      softmax(j);
+      barrier();                // #2j+3
+    };
+    int j = 0;
+    for (; j + 1 < n_kt; j += 2) {
+      tile(j, I0{});
+      tile(j + 1, I1{});
+    }
+    if (j < n_kt) {
+      tile(j, I0{});
+      ++j;
+    }
+    // phase 2n+1: P.V of the last tile
+    if (j & 1) gemm_phase(j, I1{});
+    else gemm_phase(j, I0{});
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale*m + ln(l) ------------------------
