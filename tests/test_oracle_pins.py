@@ -41,6 +41,18 @@ def pin_worked_examples() -> bool:
     return True
 
 
+def test_bruteforce_matches_worked_examples():
+    """The brute-force evaluator is pinned to the hand-worked values too."""
+    for e in json.load(open(GOLDEN))["examples"]:
+        B, H, Nq, Nk, d = e["B"], e["H"], e["Nq"], e["Nk"], e["d"]
+        O, L = oracle.attention_fwd_bruteforce(np.array(e["q"]).reshape(B, Nq, H, d),
+                                               np.array(e["k"]).reshape(B, Nk, H, d),
+                                               np.array(e["v"]).reshape(B, Nk, H, d),
+                                               e["causal"], e["scale"])
+        np.testing.assert_allclose(O.ravel(), e["o"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L.ravel(), e["lse"], rtol=0, atol=1e-12)
+
+
 def _torch_ref(q, k, v, causal, scale):
     import torch
     qt = torch.from_numpy(q).permute(0, 2, 1, 3)  # [B,H,Nq,d]
