@@ -155,28 +155,10 @@ __device__ __forceinline__ int k_swz(int key) {
   if constexpr (D == 128) return m;            // 16 chunks per 256-byte row
   else return (m >> 1) ^ (4 * (m & 1));        // 8 chunks per 128-byte row
 }
-//  V, read by transpose reads: 16 lanes touch 4 consecutive rows x 32 bytes.
-template <int D>
-__device__ __forceinline__ int v_swz(int key) {
-  const int t = key & 3;
-  if constexpr (D == 128) return 4 * t + 2 * (t >> 1);
-  else return 2 * t;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// gfx950 LDS transpose read of 4 x 16-bit values. Within each group of 16
-// lanes, lane i receives element (i % 4) of the 8-byte rows addressed by
-// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)p));
-  return __builtin_bit_cast(u32x2, r);
-}
 
 // Buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -191,12 +173,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
 }
 
 // Scheduling pins for the GEMM phase: the reads of the first AHEAD operands,
-// then for every MFMA n one MFMA followed by the reads of operand n+AHEAD
-// (two 8-byte transpose reads for a V^T operand, one 16-byte read for a K
-// operand).
+// then for every MFMA n one MFMA followed by the 16-byte read of operand
+// n+AHEAD.
 template <int N, int NPV, int NS, int AHEAD>
 struct PinInterleave {
-  static constexpr int reads_of(int n) { return n < NPV ? 2 : 1; }
+  static constexpr int reads_of(int) { return 1; }
   static constexpr int preload() {
     int r = 0;
     for (int n = 0; n < AHEAD; ++n) r += reads_of(n);
@@ -230,8 +211,13 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[TILEB];
+  // V^T tiles: row d holds the tile's 64 keys of head-dim index d (128
+  // bytes) plus 16 bytes of padding, which keeps both the transposed writes
+  // and the MFMA operand reads free of bank conflicts
+  constexpr int VT_RS = 2 * BK + 16;
+  constexpr int VTB = D * VT_RS;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_vt0[VTB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_vt1[VTB];
 
   // ---- work item: (batch, head, query tile) --------------------------------
   const int lin = blockIdx.x;
@@ -287,13 +273,12 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   const int j_end = CAUSAL ? min(n_kt, qw0 / BK + 1) : n_kt;
 
   // ---- asynchronous global -> LDS copies ------------------------------------
-  uint32_t k_off[NCPW], v_off[NCPW];
+  uint32_t k_off[NCPW];
 #pragma unroll
   for (int it = 0; it < NCPW; ++it) {
     const int row = (it * kWaves + wave) * RPI + lane / CH;
     const int pc = lane % CH;  // physical chunk in LDS
     k_off[it] = row * row_bytes + 16 * (pc ^ k_swz<D>(row));
-    v_off[it] = row * row_bytes + 16 * (pc ^ v_swz<D>(row));
   }
   auto rsrc_for = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
     const int kbase = j * BK;
@@ -305,10 +290,31 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
 #pragma unroll
     for (int it = 0; it < NCPW; ++it) dma16(r, lk + (it * kWaves + wave) * 1024, k_off[it]);
   };
-  auto issue_v = [&](int j, uint8_t* lv) __attribute__((always_inline)) {
+  // V goes through registers and is written transposed: lane (kp, dc) of
+  // the copying waves loads rows 2kp and 2kp+1 of the tile at 16-byte chunk
+  // dc and writes, for each of its 8 head-dim indices d = 8dc + i, the word
+  // (V[2kp][d], V[2kp+1][d]) to V^T row d, column kp. Each write instruction
+  // then covers two rows of opposite parity x 32 consecutive words.
+  const bool v_copier = (D == 128) || (wave < 4);
+  const int v_dc = 2 * wave + (lane >> 5);
+  const int v_kp = lane & 31;
+  const uint32_t v_src0 = (uint32_t)(2 * v_kp) * row_bytes + 16 * v_dc;
+  u32x4 vst[2];
+  auto load_v = [&](int j) __attribute__((always_inline)) {
+    if (!v_copier) return;
     const auto r = rsrc_for(Vb, j);
+    vst[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, v_src0, 0, 0));
+    vst[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, v_src0 + row_bytes, 0, 0));
+  };
+  auto store_v = [&](uint8_t* vt) __attribute__((always_inline)) {
+    if (!v_copier) return;
+    uint8_t* dst = vt + (8 * v_dc) * VT_RS + 4 * v_kp;
 #pragma unroll
-    for (int it = 0; it < NCPW; ++it) dma16(r, lv + (it * kWaves + wave) * 1024, v_off[it]);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = vst[0][i >> 1], bb = vst[1][i >> 1];
+      const uint32_t word = (i & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
+      *reinterpret_cast<uint32_t*>(dst + i * VT_RS) = word;
+    }
   };
 
   // ---- per-lane LDS read offsets (fixed for the whole kernel) ---------------
@@ -322,19 +328,9 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < DK; ++i) koff[i] = key * ROWB + 16 * ((2 * i + hf) ^ sw);
   }
-  // V transpose read: lane (g16, li) of a 16-key step reads key
-  // 8*(g16>>1) + 4r + (li>>2), 8-byte piece (li&1) of 16-byte chunk
-  // 4*db + 2*(g16&1) + ((li&3)>>1). The V swizzle depends only on li>>2, so
-  // one offset per 32-row block db serves every key step (+16 rows) and r.
-  uint32_t voff[DB];
-  {
-    const int g16 = lane >> 4, li = lane & 15;
-    const int key = 8 * (g16 >> 1) + (li >> 2);
-    const int sw = v_swz<D>(key);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      voff[db] = key * ROWB + 16 * ((4 * db + 2 * (g16 & 1) + ((li & 3) >> 1)) ^ sw) + 8 * (li & 1);
-  }
+  // V^T operand: lane (ln, hf) reads row 32*db + ln, bytes 32*ks + 16*hf
+  // (keys 16*ks + 8*hf .. +7); everything but the lane part is an immediate.
+  const uint32_t vt_off = ln * VT_RS + 16 * hf;
 
   // ---- running state -------------------------------------------------------
   f32x16 o[DB];
@@ -365,12 +361,8 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // the S^T MFMAs produce a tile nobody reads.
   auto gemm = [&](int j, const uint8_t* lk, const uint8_t* lv) __attribute__((always_inline)) {
     if (j > j_end) return;  // wave-uniform: past this wave's rows
-    uint32_t vo[DB], ko[DK];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      vo[db] = voff[db];
-      asm volatile("" : "+v"(vo[db]));
-    }
+    uint32_t vo = vt_off, ko[DK];
+    asm volatile("" : "+v"(vo));
 #pragma unroll
     for (int i = 0; i < DK; ++i) {
       ko[i] = koff[i];
@@ -382,12 +374,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       u32x4 a;
       if (n < NPV) {
         const int ks = n / DB, db = n % DB;
-        const u32x2 t0 = lds_read_tr16(lv + vo[db] + (ks * 16) * ROWB);
-        const u32x2 t1 = lds_read_tr16(lv + vo[db] + (ks * 16 + 4) * ROWB);
-        a[0] = t0[0];
-        a[1] = t0[1];
-        a[2] = t1[0];
-        a[3] = t1[1];
+        a = *reinterpret_cast<const u32x4*>(lv + vo + db * 32 * VT_RS + 32 * ks);
       } else {
         const int m = n - NPV, i = m / KB, kb = m % KB;
         a = *reinterpret_cast<const u32x4*>(lk + ko[i] + kb * 32 * ROWB);
@@ -478,51 +465,69 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // group B runs the same sequence one phase later, so on every SIMD one
   // wave issues MFMAs while the other runs its softmax. Each group has its
   // own straight-line loop; the k-th barrier of every wave pairs up.
-  // K_j is read in phases 2j and 2j+1, V_j in phases 2j+2 and 2j+3. At the
-  // start of each even phase 2m every wave starts its share of the copies of
-  // K_{m+1} and V_m, into the buffers that held K_{m-1} and V_{m-2} (last
-  // read in phase 2m-1), and waits for them just before barrier #2m+2.
+  // K_j is read in phases 2j and 2j+1, V_j in phases 2j+2 and 2j+3.
+  // * At the start of each even phase 2m every wave starts its share of the
+  //   LDS copy of K_{m+1}, into the K buffer that held K_{m-1} (last read in
+  //   phase 2m-1); it is waited for before barrier #2m+2.
+  // * At the start of each odd phase 2m+1 every copying wave writes V_m
+  //   (already in registers) transposed into the V^T buffer that held V_{m-2}
+  //   (last read in phase 2m-1), then starts loading V_{m+1} into the same
+  //   registers, two phases ahead of its write.
+  // Vector-memory loads retire in order, so before barrier #2m+2 a wait that
+  // leaves only the two newest loads (V_{m+1}) outstanding covers K_{m+1}.
   auto barrier = [&]() __attribute__((always_inline)) { __syncthreads(); };
-  auto wait_copies = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // K_{m+1} landed and this wave's V^T writes done; V_{m+1} may be in flight.
+  auto wait_k = [&](bool v_in_flight) __attribute__((always_inline)) {
+    if (v_copier && v_in_flight) __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2), lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x0070);                           // vmcnt(0), lgkmcnt(0)
   };
-  // Copies of K_{m+1} and V_m; BUF = m & 1 (compile time).
-  auto issue_pair = [&](int m, auto buf) __attribute__((always_inline)) {
+  // K_{m+1} copy into K buffer (m+1) & 1; BUF = m & 1 (compile time).
+  auto issue_k_next = [&](int m, auto buf) __attribute__((always_inline)) {
     if constexpr (decltype(buf)::value == 0) {
       if (m + 1 < n_kt) issue_k(m + 1, lds_k1);
-      if (m < n_kt) issue_v(m, lds_v0);
     } else {
       if (m + 1 < n_kt) issue_k(m + 1, lds_k0);
-      if (m < n_kt) issue_v(m, lds_v1);
     }
   };
+  // Write V_m into V^T buffer m & 1 = BUF, then start loading V_{m+1}. The
+  // V_m loads are older than the K_{m+1} copy issued at the start of phase 2m.
+  auto write_v = [&](int m, auto buf) __attribute__((always_inline)) {
+    if (m >= n_kt) return;
+    if (m + 1 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70 | NCPW);  // vmcnt(NCPW)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+    if constexpr (decltype(buf)::value == 0) store_v(lds_vt0);
+    else store_v(lds_vt1);
+    if (m + 1 < n_kt) load_v(m + 1);
+  };
   // GEMM phase of tile j with BUF = j & 1: K_j in K buffer BUF, V_{j-1} in
-  // V buffer BUF ^ 1.
+  // V^T buffer BUF ^ 1.
   auto gemm_phase = [&](int j, auto buf) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);
     if constexpr (decltype(buf)::value == 0)
-      gemm(j, lds_k0, lds_v1);
+      gemm(j, lds_k0, lds_vt1);
     else
-      gemm(j, lds_k1, lds_v0);
+      gemm(j, lds_k1, lds_vt0);
     __builtin_amdgcn_s_setprio(0);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // the first GEMM phase multiplies P = 0 with V buffer 1: make it finite
-  for (int i = tid; i < TILEB / 16; i += kThreads)
-    reinterpret_cast<u32x4*>(lds_v1)[i] = u32x4{0, 0, 0, 0};
+  // the first GEMM phase multiplies P = 0 with V^T buffer 1: make it finite
+  for (int i = tid; i < VTB / 16; i += kThreads)
+    reinterpret_cast<u32x4*>(lds_vt1)[i] = u32x4{0, 0, 0, 0};
   issue_k(0, lds_k0);
-  wait_copies();
-  barrier();  // #0
+  load_v(0);
+  wait_k(true);  // K_0 landed; V_0 may be in flight
+  barrier();     // #0
   if (grp == 0) {
     // group A: phase 2j = GEMM(j), phase 2j+1 = softmax(j)
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
-      issue_pair(j, buf);       // start of phase 2j
+      issue_k_next(j, buf);     // start of phase 2j
       gemm_phase(j, buf);
       barrier();                // #2j+1
+      write_v(j, buf);          // start of phase 2j+1
       softmax(j);
-      wait_copies();
+      wait_k(j + 1 < n_kt);
       barrier();                // #2j+2
     };
     int j = 0;
@@ -540,16 +545,17 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     barrier();
   } else {
     // group B: phase 2j+1 = GEMM(j), phase 2j+2 = softmax(j)
-    issue_pair(0, I0{});        // start of phase 0
+    issue_k_next(0, I0{});      // start of phase 0
     barrier();                  // #1
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
+      write_v(j, buf);          // start of phase 2j+1
       gemm_phase(j, buf);
-      wait_copies();
+      wait_k(j + 1 < n_kt);
       barrier();                // #2j+2
       if constexpr (decltype(buf)::value == 0)
-        issue_pair(j + 1, I1{});  // start of phase 2j+2
+        issue_k_next(j + 1, I1{});  // start of phase 2j+2
       else
-        issue_pair(j + 1, I0{});
+        issue_k_next(j + 1, I0{});
       softmax(j);
       barrier();                // #2j+3
     };
