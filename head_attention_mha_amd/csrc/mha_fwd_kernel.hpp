@@ -156,6 +156,23 @@ __device__ __forceinline__ int k_swz(int key) {
   else return (m >> 1) ^ (4 * (m & 1));        // 8 chunks per 128-byte row
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// max / sum of x over lanes l and l ^ 32, in both lanes: one v_permlane32_swap
+// (a VALU op) instead of a shuffle through LDS. With both operands x, the
+// swap returns x of lanes 0-31 in every lane (first result) and x of lanes
+// 32-63 in every lane (second result). The results are read as plain
+// integers first: __builtin_bit_cast of a vector element reads element 0.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -421,12 +438,18 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
           s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // two independent max chains (one per 32-key block), then across halves
+    float mk[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      mk[kb] = s[kb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 1; r < 16; ++r) mk[kb] = fmaxf(mk[kb], s[kb][r]);
+    }
+    float mx = mk[0];
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mk[kb]);
+    mx = max_halves(mx);
     // the O and l rescale is deferred while the max stays within
     // kDeferLog2 of the reference max
     if (__any(mx > m_run + p.defer_raw)) {
@@ -445,17 +468,21 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
     // P^T fragments: k-step ks covers keys 16*ks + 8*hf + 0..7
-    float rsum = 0.f;
+    // row sum in PK independent chains (one per k-step)
+    float rsum[PK];
 #pragma unroll
     for (int ks = 0; ks < PK; ++ks) {
       const int kb = ks >> 1, r0 = 8 * (ks & 1);
+      rsum[ks] = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         pf[ks][t] = O_::pack(s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1]);
-        rsum = O_::sum2(pf[ks][t], s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1], rsum);
+        rsum[ks] = O_::sum2(pf[ks][t], s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1], rsum[ks]);
       }
     }
-    l_run += rsum;
+#pragma unroll
+    for (int ks = 1; ks < PK; ++ks) rsum[0] += rsum[ks];
+    l_run += rsum[0];
   };
 
   // ---- phase schedule ------------------------------------------------------
@@ -574,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale*m + ln(l) ------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (my_q < p.Nq) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = Ob + (size_t)my_q * rs;
