@@ -502,7 +502,17 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   //   registers, two phases ahead of its write.
   // Vector-memory loads retire in order, so before barrier #2m+2 a wait that
   // leaves only the two newest loads (V_{m+1}) outstanding covers K_{m+1}.
-  auto barrier = [&]() __attribute__((always_inline)) { __syncthreads(); };
+  // Workgroup barrier without a memory fence: __syncthreads() also releases
+  // memory at workgroup scope, which would make each wave wait at every
+  // barrier for the K copy it started at the beginning of the phase. The
+  // waits that matter are explicit (wait_k: the copies the next phase reads
+  // and this wave's LDS writes); the empty asm statements keep the compiler
+  // from moving LDS accesses across the barrier.
+  auto barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   // K_{m+1} landed and this wave's V^T writes done; V_{m+1} may be in flight.
   auto wait_k = [&](bool v_in_flight) __attribute__((always_inline)) {
     if (v_copier && v_in_flight) __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2), lgkmcnt(0)
