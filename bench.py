@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -34,9 +35,14 @@ KERNEL_SOURCES = [
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so
+    that editing a comment does not invalidate counters taken on the code."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+        text = open(p, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -40,12 +40,15 @@
 //   consecutive keys per 16-key step -- exactly the B-operand fragment of the
 //   P.V product, so P needs no cross-lane layout change ("SparkAttention"
 //   step 3 becomes a register-local conversion).
-// * K and V tiles are copied global -> LDS by buffer loads that write LDS
+// * K tiles are copied global -> LDS by buffer loads that write LDS
 //   directly (no staging registers); rows past the end of the keys read as
 //   zero through the buffer's range check, so the tail needs no branches.
-//   Copies run two phases ahead of their first use.
-// * V stays row-major in LDS; the V^T operand of the P.V product comes from
-//   gfx950 LDS transpose reads (ds_read_b64_tr_b16), two per MFMA.
+// * V tiles go through registers (loaded two phases ahead) and are written
+//   transposed into a padded V^T tile, so the V^T operand of the P.V
+//   product is one 16-byte LDS read per MFMA like the K operand.
+// * The row max is exchanged between the two lane halves with
+//   v_permlane32_swap; barriers are bare s_barrier instructions with the
+//   needed waits made explicit.
 // * LDS tiles are XOR-swizzled in 16-byte units so the MFMA operand reads
 //   are free of bank conflicts; the GEMM phase reads each operand four MFMAs
 //   ahead of its use.
