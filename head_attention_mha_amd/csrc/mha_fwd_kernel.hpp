@@ -55,10 +55,10 @@
 // * The O rescale is deferred while a row's max stays within 2^8 (exp2
 //   domain) of the max O and l were last scaled to; O/l and LSE are the same
 //   in exact arithmetic, and the rescale then runs only when the max jumps.
-// * The 1-D grid is remapped so that consecutive work items of one head land
-//   on the same XCD (workgroups are dispatched round-robin over the 8 XCDs),
-//   keeping a head's K/V in that XCD's L2; causal query tiles run heaviest
-//   first.
+// * The 1-D grid is remapped so that all query tiles of a head run on one
+//   XCD (workgroups are dispatched round-robin over the 8 XCDs), keeping the
+//   head's K/V in that XCD's L2, and so that each XCD starts its heaviest
+//   causal query tiles (of all its heads) first.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -240,12 +240,22 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_vt1[VTB];
 
   // ---- work item: (batch, head, query tile) --------------------------------
+  // Workgroups are dispatched in index order, round-robin over the 8 XCDs.
+  // When the heads split evenly over the XCDs, XCD x takes the heads
+  // bh = 8*i + x (a head's K/V then stays in one XCD's L2) and its k-th
+  // workgroup takes query-tile rank k / (heads per XCD) of head rank
+  // k % (heads per XCD); otherwise the same order runs over all heads. For
+  // causal attention query-tile rank 0 is the last (heaviest) query tile, so
+  // every XCD starts its heaviest work first.
   const int lin = blockIdx.x;
-  int w = lin;
-  if ((p.n_blocks & 7) == 0) w = (lin & 7) * (p.n_blocks >> 3) + (lin >> 3);
-  const int bh = w / p.n_qtiles;
-  int qt = w - bh * p.n_qtiles;
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest tiles first
+  const int BH = p.B * p.H;
+  const bool by_xcd = (BH & 7) == 0;
+  const int k = by_xcd ? lin >> 3 : lin;
+  const int nh = by_xcd ? BH >> 3 : BH;
+  const int qi = k / nh;
+  const int hh = k - qi * nh;
+  const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;
+  const int qt = CAUSAL ? p.n_qtiles - 1 - qi : qi;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int q0 = qt * kBQ;
