@@ -1,4 +1,4 @@
-"""CPU fp64 oracle for the fused MHA forward.
+"""CPU fp64 oracle for the fused MHA forward and its backward.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it; the product path must not.
@@ -13,3 +13,4 @@ from .attention import (  # noqa: F401
     weighted_values,
     log_sum_exp,
 )
+from .backward import attention_bwd, softmax_grad  # noqa: F401
