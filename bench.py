@@ -1,12 +1,14 @@
-"""Benchmark of the fused MHA forward on one MI355X.
+"""Benchmark of the fused MHA forward (default) or backward on one MI355X.
 
-A step is one mha_fwd call over the whole workload (inputs already resident
-in HBM). Default workload: B=1, H=8, Nq=Nk=16384, d=128, bf16, causal (the
-long-sequence small-batch regime of the FlashAttention long-sequence post).
-Prints ONE JSON line.
+A step is one mha_fwd call (``--pass fwd``) or one mha_bwd call (``--pass
+bwd``: D, dQ and dK/dV, from the forward's O and LSE computed beforehand)
+over the whole workload, inputs already resident in HBM. Default workload:
+B=1, H=8, Nq=Nk=16384, d=128, bf16, causal (the long-sequence small-batch
+regime of the FlashAttention long-sequence post). Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
-                  [--no-cpu-baseline] [--cpu-seconds S] [--calib-copy-mib M]
+                  [--pass fwd|bwd] [--no-cpu-baseline] [--cpu-seconds S]
+                  [--calib-copy-mib M]
 """
 from __future__ import annotations
 
@@ -27,18 +29,23 @@ sys.path.insert(0, ROOT)
 import workloads as wl  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak (B=1,H=8,N=16k,d=128 causal)"
+METRIC_BWD = ("attention bwd TFLOP/s (5-matmul count 10*B*H*Nq*Nk*d, halved causal) and % of "
+              "MFMA bf16 peak")
 PEAK_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 MFMA peak
 KERNEL_SOURCES = [
     os.path.join(ROOT, "head_attention_mha_amd", "csrc", "mha_fwd_kernel.hpp"),
     os.path.join(ROOT, "head_attention_mha_amd", "csrc", "mha_api.hip"),
 ]
+KERNEL_SOURCES_BWD = KERNEL_SOURCES + [
+    os.path.join(ROOT, "head_attention_mha_amd", "csrc", "mha_bwd_kernel.hpp"),
+]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     """Hash of the kernel sources with comments and whitespace removed, so
     that editing a comment does not invalidate counters taken on the code."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         text = open(p, encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
@@ -46,10 +53,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def hbm_traffic(workload: str):
+def hbm_traffic(workload: str, which: str = "fwd"):
     """Per-launch HBM bytes (FETCH + WRITE) from the committed counter summary,
     or None when there is none or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    name = f"hbm_traffic_{workload}.txt" if which == "fwd" else f"hbm_traffic_bwd_{workload}.txt"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -57,7 +65,8 @@ def hbm_traffic(workload: str):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+    srcs = KERNEL_SOURCES if which == "fwd" else KERNEL_SOURCES_BWD
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(srcs):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -105,12 +114,58 @@ def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float) -> dict:
     }
 
 
+def cpu_baseline_bwd(w: wl.Workload, qb, kb, vb, gb, target_s: float) -> dict:
+    """The fp64 backward oracle, as it stands, on a bounded sample.
+
+    The sample is the first n tokens (queries and keys) of the first m heads
+    of batch entry 0: a prefix of a sequence is a complete problem of the
+    same kind (causal stays causal). n grows until one head takes about a
+    quarter of ``target_s`` or covers the whole sequence; then whole heads
+    are added while the time stays within ``target_s``."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
+                      if i.get("user_api") == "blas") or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, k, v, do = (wl.bits_to_f64(x[:1], w.dtype) for x in (qb, kb, vb, gb))
+
+    def timed(n, m):
+        nk = n if w.Nq == w.Nk else w.Nk
+        t0 = time.perf_counter()
+        oracle.attention_bwd(q[:, :n, :m], k[:, :nk, :m], v[:, :nk, :m], do[:, :n, :m],
+                             w.causal, w.scale)
+        return time.perf_counter() - t0, nk
+
+    n, m = min(w.Nq, 256), 1
+    t, nk = timed(n, m)
+    while n < w.Nq and t < target_s / 4:
+        n = min(w.Nq, int(n * 1.6))
+        t, nk = timed(n, m)
+    if n == w.Nq and w.H > 1:
+        m = int(max(1, min(w.H, target_s / max(t, 1e-6))))
+        if m > 1:
+            t, nk = timed(n, m)
+    flops = 10.0 * n * nk * w.d * m / (2.0 if w.causal else 1.0)
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"the first {n} queries and {nk} keys of heads 0..{m - 1} of batch entry 0, "
+                   f"fp64 NumPy, {t:.1f} s; FLOPs counted as for the GPU line"),
+        "seconds": t,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_causal", choices=list(wl.WORKLOADS))
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -142,10 +197,28 @@ def main() -> int:
     argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             w.B, w.H, w.Nq, w.Nk, w.d, int(w.causal), w.scale, sp, dt)
 
-    def step():
+    def fwd_step():
         st = mha.mha_fwd(*argv)
         if st != mha.MHA_OK:
             raise mha.MhaError(st)
+
+    step = fwd_step
+    if args.which == "bwd":
+        gb = wl.make_grad(w)
+        g = to_device(torch, gb, w.dtype)
+        fwd_step()  # O and LSE the backward starts from (not timed)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty_like(lse)
+        bargv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(),
+                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                 w.B, w.H, w.Nq, w.Nk, w.d, int(w.causal), w.scale, sp, dt)
+
+        def bwd_step():
+            st = mha.mha_bwd(*bargv)
+            if st != mha.MHA_OK:
+                raise mha.MhaError(st, "mha_bwd")
+
+        step = bwd_step
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 2
@@ -176,12 +249,12 @@ def main() -> int:
     total_ms = ev[0].elapsed_time(ev[K])
     ms_per_step = total_ms / K
 
-    flops = w.flops
+    flops = w.flops if args.which == "fwd" else 2.5 * w.flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (per.mean() * 1e-3) / 1e12
-    traffic = hbm_traffic(w.name)
+    traffic = hbm_traffic(w.name, args.which)
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
@@ -194,7 +267,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+        "config": {"workload": w.name, "pass": args.which, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "io_dtype": w.dtype, "accumulate": "fp32",
                    "flops_per_step": flops},
         "roofline": {
@@ -204,18 +277,23 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "mha_fwd_kernel",
+            "kernel": ("mha_fwd_kernel" if args.which == "fwd" else
+                       "mha_bwd (delta, dq and dkdv kernels, one call)"),
             "launch_ms": {"mean": round(float(per.mean()), 5), "median": round(float(np.median(per)), 5),
                           "min": round(float(per.min()), 5)},
         },
         "timed_wall_s": round(wall, 3),
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(
+            KERNEL_SOURCES if args.which == "fwd" else KERNEL_SOURCES_BWD),
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
         print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
               flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
+        if args.which == "fwd":
+            line["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
+        else:
+            line["cpu_baseline"] = cpu_baseline_bwd(w, qb, kb, vb, gb, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

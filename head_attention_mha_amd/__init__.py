@@ -1,4 +1,4 @@
-"""Fused multi-head attention forward for AMD MI355X (gfx950).
+"""Fused multi-head attention forward and backward for AMD MI355X (gfx950).
 
 The computation lives in the HIP library ``libmha.so`` behind the C ABI of
 include/mha.h; this package only binds it (see ``_binding``).
@@ -15,8 +15,10 @@ from ._binding import (  # noqa: F401
     MHA_OK,
     MhaError,
     attention,
+    attention_backward,
     load_library,
     mha_abi_version,
+    mha_bwd,
     mha_fwd,
     mha_status_string,
 )

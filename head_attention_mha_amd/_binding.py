@@ -1,9 +1,10 @@
 """ctypes binding of libmha.so (argument marshalling only).
 
-The names follow include/mha.h. ``mha_fwd`` takes raw device pointers and
-sizes exactly like the C entry point; ``attention`` is a convenience wrapper
-that takes PyTorch device tensors, allocates O and LSE with PyTorch and calls
-``mha_fwd`` on the current stream. Every step of the computation runs in the
+The names follow include/mha.h. ``mha_fwd`` and ``mha_bwd`` take raw device
+pointers and sizes exactly like the C entry points; ``attention`` and
+``attention_backward`` are convenience wrappers that take PyTorch device
+tensors, allocate the outputs with PyTorch and call the entry point on the
+current stream. Every step of the computation runs in the
 HIP kernel; if the library is missing this module raises instead of
 computing anything another way.
 """
@@ -25,15 +26,15 @@ MHA_DTYPE_FP16 = 0
 MHA_DTYPE_BF16 = 1
 
 # Every symbol include/mha.h declares.
-EXPORTED_SYMBOLS = ("mha_fwd", "mha_status_string", "mha_abi_version")
+EXPORTED_SYMBOLS = ("mha_fwd", "mha_bwd", "mha_status_string", "mha_abi_version")
 
 _lib = None
 
 
 class MhaError(RuntimeError):
-    def __init__(self, status: int):
+    def __init__(self, status: int, entry: str = "mha_fwd"):
         self.status = status
-        super().__init__(f"mha_fwd failed: {mha_status_string(status)} (status {status})")
+        super().__init__(f"{entry} failed: {mha_status_string(status)} (status {status})")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -48,6 +49,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.mha_fwd.restype = ctypes.c_int
     lib.mha_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+    ]
+    lib.mha_bwd.restype = ctypes.c_int
+    lib.mha_bwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
@@ -75,6 +83,67 @@ def mha_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, N
                                       float(scale), stream, int(dtype)))
 
 
+def mha_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+            delta: int, B: int, H: int, Nq: int, Nk: int, d: int, causal: int, scale: float,
+            stream: int | None, dtype: int) -> int:
+    """Call the C entry point with raw pointers; returns the status code."""
+    return int(load_library().mha_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, d,
+                                      int(causal), float(scale), stream, int(dtype)))
+
+
+def _check_qkv(q, k, v):
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, N, H, d]")
+    B, Nq, H, d = q.shape
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one GPU device")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    return B, Nq, H, d, k.shape[1]
+
+
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                       stream=None):
+    """dQ, dK, dV, D = attention_backward(Q, K, V, O, LSE, dO) for device tensors.
+
+    q, o, dout: [B, Nq, H, d]; k, v: [B, Nk, H, d]; one dtype (float16 or
+    bfloat16), contiguous, on one HIP device; lse: [B, H, Nq] float32 as
+    written by ``attention``. Returns (dq, dk, dv) in the input dtype and
+    D = rowsum(dO * O) as float32 [B, H, Nq]. ``scale`` defaults to 1/sqrt(d)
+    and must be the forward's.
+    """
+    import torch
+
+    B, Nq, H, d, Nk = _check_qkv(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    dt = MHA_DTYPE_BF16 if q.dtype == torch.bfloat16 else MHA_DTYPE_FP16
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = mha_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                     B, H, Nq, Nk, d, int(bool(causal)), float(scale), stream, dt)
+    if st != MHA_OK:
+        raise MhaError(st, "mha_bwd")
+    return dq, dk, dv, delta
+
+
 def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
               stream=None):
     """O, LSE = attention(Q, K, V) for PyTorch device tensors.
@@ -85,18 +154,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     """
     import torch
 
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, N, H, d]")
-    B, Nq, H, d = q.shape
-    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != d or v.shape != k.shape:
-        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
-    Nk = k.shape[1]
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
-        raise ValueError("q, k, v must share dtype float16 or bfloat16")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda) or not (q.device == k.device == v.device):
-        raise ValueError("q, k, v must be on one GPU device")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    B, Nq, H, d, Nk = _check_qkv(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:

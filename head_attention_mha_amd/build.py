@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmha.so")
 SOURCES = [os.path.join(CSRC, "mha_api.hip")]
-DEPS = [os.path.join(CSRC, "mha_fwd_kernel.hpp"), os.path.join(ROOT, "include", "mha.h")]
+DEPS = [os.path.join(CSRC, "mha_fwd_kernel.hpp"), os.path.join(CSRC, "mha_bwd_kernel.hpp"),
+        os.path.join(ROOT, "include", "mha.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

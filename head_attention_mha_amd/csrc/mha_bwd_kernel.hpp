@@ -1,0 +1,575 @@
+// Attention backward for gfx950 (CDNA4): dQ, dK and dV of the fused forward.
+//
+// The forward is recomputed tile by tile from the stored LSE, P = exp(S -
+// LSE) ("StreamKL", Methodology section 2), never materialising the Nq x Nk
+// matrices. With D_i = sum_c dO_ic O_ic (the per-row term the SparkAttention
+// backward passage calls dPsum) the gradients are
+//
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
+//   dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Three kernels, each owning its outputs (no atomics, no workspace):
+// * mha_bwd_delta_kernel: D, one group of d/8 lanes per query row.
+// * mha_bwd_dkdv_kernel: column-parallel, as the pages' backward workers are
+//   (the FlashAttention long-sequence post, "Attention parallelism"; the
+//   SparkAttention backward passage): each wave owns 32 keys, streams the
+//   Q/dO tiles that see them and accumulates their dK and dV in registers.
+// * mha_bwd_dq_kernel: row-parallel, like the forward: each wave owns 32
+//   query rows and streams K/V tiles. The pages add dQ across column workers
+//   with atomics; "StreamKL" (Methodology section 2) also describes separate
+//   kernels for when the dQ buffer does not fit in L2. Separate kernels are
+//   used here always: S and dP are computed once more, but dQ needs neither
+//   atomics nor an fp32 buffer, and the result is deterministic.
+//
+// Layouts mirror the forward so that no operand needs a cross-lane move:
+// the score tile is computed with the query (dq) or key (dkdv) index on the
+// MFMA columns, i.e. one query/key per lane, and the rows of the other
+// operand are fed in the order of k_row_order, which leaves every lane
+// holding 8 consecutive keys/queries per 16-step -- exactly the B-operand
+// fragment of the following product. The transposed operands (K^T for dQ,
+// dO^T and Q^T for dV and dK) come from gfx950 LDS transpose reads.
+#pragma once
+
+#include "mha_fwd_kernel.hpp"
+
+namespace mha {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;
+  int B, H, Nq, Nk;
+  float scale;       // softmax scale (> 0)
+  float scale_log2;  // scale * log2(e)
+  int n_blocks;      // workgroups launched
+  int n_tiles;       // query blocks (dq) or key blocks (dkdv) per (b, h)
+};
+
+namespace bwd {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBQ = 32 * kWaves;   // query rows per dq workgroup
+constexpr int kBKV = 32 * kWaves;  // keys per dkdv workgroup
+constexpr int kBK = 64;            // keys per tile streamed by dq
+constexpr int kBQt = 32;           // queries per tile streamed by dkdv
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS transpose read of 4 x 16-bit values: within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte pieces addressed by lanes i/4,
+// 4 + i/4, 8 + i/4 and 12 + i/4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* ptr) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)ptr));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Per-lane byte offsets of the transpose reads that form the A operand
+// "rows = head-dim index 32*db + (lane % 32), k-slots = 8 consecutive tile
+// rows 16*ks + 8*(lane / 32) + 0..7" from a row-major tile whose 16-byte
+// chunks are swizzled by k_swz<D> of the row: two reads per operand, the
+// second 4 rows further (r = 0, 1). Lane (g, a) of 16-lane group g supplies
+// the 8-byte piece of row 8*(g/2) + 4r + a/4 at head-dim index
+// 32*db + 16*(g%2) + 4*(a%4). Everything but these offsets (the 16-row step
+// ks) is an immediate, since the swizzle depends on the row's low 4 bits.
+template <int D>
+__device__ __forceinline__ uint32_t tr_off(int lane, int db, int r) {
+  constexpr int ROWB = 2 * D;
+  const int g = lane >> 4, a = lane & 15;
+  const int row = 8 * (g >> 1) + 4 * r + (a >> 2);
+  const int chunk = 4 * db + 2 * (g & 1) + ((a & 3) >> 1);
+  return row * ROWB + 16 * (chunk ^ k_swz<D>(row)) + 8 * (a & 1);
+}
+
+// Two packed 16-bit values -> fp32.
+template <typename T>
+__device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+  if constexpr (std::is_same<T, BF16>::value) {
+    return f32x2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
+  } else {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+  }
+}
+
+// One wave copies 256 bytes global -> LDS: lane l's 4 bytes at `voffset`
+// land at lds_dst + 4*l (per-dword range check: lanes past the end get 0).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)((lds_u8*)lds_dst),
+                                           4, voffset, 0, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (a fenced barrier would also wait
+// for this wave's copy of the next tile). The waits that matter are explicit
+// before it; the empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The 8 values of one transposed A operand.
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* base, uint32_t off0, uint32_t off1) {
+  const u32x2 t0 = lds_read_tr16(base + off0);
+  const u32x2 t1 = lds_read_tr16(base + off1);
+  return u32x4{t0[0], t0[1], t1[0], t1[1]};
+}
+
+}  // namespace bwd
+
+// ---- D = rowsum(dO o O) ------------------------------------------------------
+// One group of D/8 lanes per query row (16 bytes per lane, contiguous), rows
+// ordered as D is stored: r = (b*H + h)*Nq + i.
+template <typename T, int D>
+__global__ __launch_bounds__(bwd::kThreads) void mha_bwd_delta_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;                    // lanes per row
+  constexpr int RPB = bwd::kThreads / LPR;      // rows per workgroup
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + tid / LPR;
+  const long long n_rows = (long long)p.B * p.H * p.Nq;
+  const int part = tid % LPR;
+  float acc = 0.f;
+  if (row < n_rows) {
+    const long long bh = row / p.Nq;
+    const int i = (int)(row - bh * p.Nq);
+    const int b = (int)(bh / p.H), h = (int)(bh - (long long)b * p.H);
+    const size_t off = (((size_t)b * p.Nq + i) * p.H + h) * D + 8 * part;
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(p.o + off);
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(p.dout + off);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x2 a = bwd::unpack2<T>(ov[w]);
+      const f32x2 g = bwd::unpack2<T>(gv[w]);
+      acc = __builtin_fmaf(a[0], g[0], acc);
+      acc = __builtin_fmaf(a[1], g[1], acc);
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < n_rows && part == 0) p.delta[row] = acc;
+}
+
+// ---- dQ: row-parallel ----------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) {
+  using O_ = Ops<T>;
+  constexpr int BK = bwd::kBK;
+  constexpr int kBQ = bwd::kBQ;
+  constexpr int NW = bwd::kWaves;
+  constexpr int KB = BK / 32;            // 32-key blocks per tile
+  constexpr int DK = D / 16;             // k-steps over the head dim
+  constexpr int DB = D / 32;             // 32-row blocks of dQ^T
+  constexpr int PK = BK / 16;            // 16-key steps of dQ^T += K^T dS^T
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BK * ROWB;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int NCPW = TILEB / 1024 / NW;  // 1 KiB copies per wave per tensor
+  static_assert(NCPW >= 1 && (NW * RPI) % 16 == 0, "copy layout");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[TILEB];
+
+  // work item: (batch, head, query block); a head's blocks on one XCD when
+  // the heads split evenly over the 8 XCDs, heaviest causal blocks first
+  const int lin = blockIdx.x;
+  const int BH = p.B * p.H;
+  const bool by_xcd = (BH & 7) == 0;
+  const int kk = by_xcd ? lin >> 3 : lin;
+  const int nh = by_xcd ? BH >> 3 : BH;
+  const int qi = kk / nh;
+  const int hh = kk - qi * nh;
+  const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;
+  const int qt = CAUSAL ? p.n_tiles - 1 - qi : qi;
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int q0 = qt * kBQ;
+
+  const size_t rs = (size_t)p.H * D;
+  const size_t qo = ((size_t)b * p.Nq * p.H + h) * D;
+  const size_t kvo = ((size_t)b * p.Nk * p.H + h) * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hf = lane >> 5;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + ln;
+
+  // Q and dO fragments (B operands), read once; LSE (log2 units) and D
+  u32x4 qf[DK], gf[DK];
+  float lse2 = 0.f, dlt = 0.f;
+  if (my_q < p.Nq) {
+    const uint16_t* qrow = p.q + qo + (size_t)my_q * rs + 8 * hf;
+    const uint16_t* grow = p.dout + qo + (size_t)my_q * rs + 8 * hf;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+      qf[i] = *reinterpret_cast<const u32x4*>(qrow + 16 * i);
+      gf[i] = *reinterpret_cast<const u32x4*>(grow + 16 * i);
+    }
+    lse2 = p.lse[(size_t)bh * p.Nq + my_q] * bwd::kLog2e;
+    dlt = p.delta[(size_t)bh * p.Nq + my_q];
+  } else {
+#pragma unroll
+    for (int i = 0; i < DK; ++i) qf[i] = gf[i] = u32x4{0, 0, 0, 0};
+  }
+
+  // key tiles
+  const int n_ktiles_all = (p.Nk + BK - 1) / BK;
+  int n_kt = n_ktiles_all;
+  if (CAUSAL) n_kt = min(n_ktiles_all, (min(p.Nq, q0 + kBQ) + BK - 1) / BK);
+  int jm = (p.Nk % BK) ? p.Nk / BK : n_ktiles_all;  // tiles [0, jm) need no mask
+  if (CAUSAL) jm = min(jm, (qw0 + 1) / BK);
+  const int j_end = CAUSAL ? min(n_kt, qw0 / BK + 1) : n_kt;  // this wave's last tile + 1
+
+  // K and V tiles: LDS copies, rows swizzled in 16-byte chunks by k_swz
+  uint32_t c_off[NCPW];
+#pragma unroll
+  for (int c = 0; c < NCPW; ++c) {
+    const int row = (c * NW + wave) * RPI + lane / CH;
+    c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ k_swz<D>(row));
+  }
+  auto issue = [&](int j, uint8_t* lk, uint8_t* lv) __attribute__((always_inline)) {
+    const int nvalid = min(BK, p.Nk - j * BK);
+    const uint32_t bytes = (uint32_t)(nvalid - 1) * row_bytes + ROWB;
+    const auto rk = make_rsrc(p.k + kvo + (size_t)j * BK * rs, bytes);
+    const auto rv = make_rsrc(p.v + kvo + (size_t)j * BK * rs, bytes);
+#pragma unroll
+    for (int c = 0; c < NCPW; ++c) dma16(rk, lk + (c * NW + wave) * 1024, c_off[c]);
+#pragma unroll
+    for (int c = 0; c < NCPW; ++c) dma16(rv, lv + (c * NW + wave) * 1024, c_off[c]);
+  };
+
+  // LDS read offsets: row operands (K and V rows in MFMA row order) and the
+  // transposed K^T operand
+  uint32_t roff[DK];
+  {
+    const int key = k_row_order(ln);
+    const int sw = k_swz<D>(key);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) roff[i] = key * ROWB + 16 * ((2 * i + hf) ^ sw);
+  }
+  uint32_t toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) toff[db][r] = bwd::tr_off<D>(lane, db, r);
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+  const float c = p.scale_log2;
+
+  auto tile = [&](int j, const uint8_t* lk, const uint8_t* lv) __attribute__((always_inline)) {
+    if (j >= j_end) return;  // wave-uniform: past this wave's rows
+    // S^T = K Q^T and dP^T = V dO^T (keys on MFMA rows, one query per lane)
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + roff[i] + kb * 32 * ROWB);
+        const u32x4 va = *reinterpret_cast<const u32x4*>(lv + roff[i] + kb * 32 * ROWB);
+        s[kb] = O_::mfma(ka, qf[i], s[kb]);
+        dp[kb] = O_::mfma(va, gf[i], dp[kb]);
+      }
+    // P = exp(scale*s - LSE), dS = P o (dP - D); element r of block kb is key
+    // j*BK + 32*kb + 16*(r>>3) + 8*hf + (r&7)
+    const int k0 = j * BK;
+    const bool masked = j >= jm;
+    u32x4 pf[PK];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
+        if (masked) {
+          const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
+          const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
+          pv = vis ? pv : 0.f;
+        }
+        e[r] = pv * (dp[kb][r] - dlt);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          pf[2 * kb + half][t] = O_::pack(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int ks = 0; ks < PK; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4 a = bwd::tr_operand(lk + ks * 16 * ROWB, toff[db][0], toff[db][1]);
+        dq[db] = O_::mfma(a, pf[ks], dq[db]);
+      }
+  };
+
+  // One barrier per tile: tile j waits for its own copies (vmcnt) and for
+  // this wave's LDS reads of tile j-1 (lgkmcnt); after the barrier every
+  // wave is done with tile j-1's buffers, which then take tile j+1.
+  issue(0, lds_k0, lds_v0);
+  for (int j = 0; j < n_kt; ++j) {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    bwd::bare_barrier();
+    const bool more = j + 1 < n_kt;
+    if (j & 1) {
+      if (more) issue(j + 1, lds_k0, lds_v0);
+      tile(j, lds_k1, lds_v1);
+    } else {
+      if (more) issue(j + 1, lds_k1, lds_v1);
+      tile(j, lds_k0, lds_v0);
+    }
+  }
+
+  // dQ = scale * dQ^T, rounded to the I/O type
+  if (my_q < p.Nq) {
+    uint16_t* row = p.dq + qo + (size_t)my_q * rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 w2;
+        w2[0] = O_::pack(dq[db][4 * a + 0] * p.scale, dq[db][4 * a + 1] * p.scale);
+        w2[1] = O_::pack(dq[db][4 * a + 2] * p.scale, dq[db][4 * a + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(row + db * 32 + 8 * a + 4 * hf) = w2;
+      }
+  }
+}
+
+// ---- dK, dV: column-parallel ---------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p) {
+  using O_ = Ops<T>;
+  constexpr int BQt = bwd::kBQt;
+  constexpr int kBKV = bwd::kBKV;
+  constexpr int NW = bwd::kWaves;
+  constexpr int DK = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int PK = BQt / 16;           // 16-query steps of dV^T / dK^T
+  constexpr int CH = D / 8;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BQt * ROWB;      // Q or dO tile
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int NCPW = TILEB / 1024 / NW;
+  static_assert(NCPW >= 1 && (NW * RPI) % 16 == 0, "copy layout");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_q0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_q1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_g0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_g1[TILEB];
+  // LSE (copied by wave 0) and D (wave 1) of the tile's queries: one 256-byte
+  // copy each, of which the first 128 bytes are the 32 values
+  __shared__ __attribute__((aligned(256))) float lds_l0[64];
+  __shared__ __attribute__((aligned(256))) float lds_l1[64];
+  __shared__ __attribute__((aligned(256))) float lds_d0[64];
+  __shared__ __attribute__((aligned(256))) float lds_d1[64];
+
+  // work item: (batch, head, key block), a head's blocks on one XCD
+  const int lin = blockIdx.x;
+  const int BH = p.B * p.H;
+  const bool by_xcd = (BH & 7) == 0;
+  const int kk = by_xcd ? lin >> 3 : lin;
+  const int nh = by_xcd ? BH >> 3 : BH;
+  const int ki = kk / nh;
+  const int hh = kk - ki * nh;
+  const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;
+  const int kt = ki;  // key block; causal: later blocks see fewer queries
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int k0 = kt * kBKV;
+
+  const size_t rs = (size_t)p.H * D;
+  const size_t qo = ((size_t)b * p.Nq * p.H + h) * D;
+  const size_t kvo = ((size_t)b * p.Nk * p.H + h) * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hf = lane >> 5;
+  const int kw0 = k0 + wave * 32;
+  const int my_k = kw0 + ln;
+
+  // K and V fragments of this wave's keys (B operands), read once
+  u32x4 kf[DK], vf[DK];
+  if (my_k < p.Nk) {
+    const uint16_t* krow = p.k + kvo + (size_t)my_k * rs + 8 * hf;
+    const uint16_t* vrow = p.v + kvo + (size_t)my_k * rs + 8 * hf;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+      kf[i] = *reinterpret_cast<const u32x4*>(krow + 16 * i);
+      vf[i] = *reinterpret_cast<const u32x4*>(vrow + 16 * i);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DK; ++i) kf[i] = vf[i] = u32x4{0, 0, 0, 0};
+  }
+
+  // query tiles: causal blocks start at the first query that sees key k0
+  const int n_qtiles_all = (p.Nq + BQt - 1) / BQt;
+  const int t_begin = CAUSAL ? min(k0 / BQt, n_qtiles_all) : 0;
+
+  uint32_t c_off[NCPW];
+#pragma unroll
+  for (int c = 0; c < NCPW; ++c) {
+    const int row = (c * NW + wave) * RPI + lane / CH;
+    c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ k_swz<D>(row));
+  }
+  // copies per wave per tile: NCPW each of Q and dO, plus LSE on wave 0 and
+  // D on wave 1
+  auto issue = [&](int t, uint8_t* lq, uint8_t* lg, float* ll, float* ld) __attribute__((always_inline)) {
+    const int nvalid = min(BQt, p.Nq - t * BQt);
+    const uint32_t bytes = (uint32_t)(nvalid - 1) * row_bytes + ROWB;
+    const auto rq = make_rsrc(p.q + qo + (size_t)t * BQt * rs, bytes);
+    const auto rg = make_rsrc(p.dout + qo + (size_t)t * BQt * rs, bytes);
+#pragma unroll
+    for (int c = 0; c < NCPW; ++c) dma16(rq, lq + (c * NW + wave) * 1024, c_off[c]);
+#pragma unroll
+    for (int c = 0; c < NCPW; ++c) dma16(rg, lg + (c * NW + wave) * 1024, c_off[c]);
+    if (wave == 0) {
+      const auto rl = make_rsrc(p.lse + (size_t)bh * p.Nq + t * BQt, (uint32_t)nvalid * 4);
+      bwd::dma4(rl, reinterpret_cast<uint8_t*>(ll), 4 * lane);
+    } else if (wave == 1) {
+      const auto rd = make_rsrc(p.delta + (size_t)bh * p.Nq + t * BQt, (uint32_t)nvalid * 4);
+      bwd::dma4(rd, reinterpret_cast<uint8_t*>(ld), 4 * lane);
+    }
+  };
+
+  uint32_t roff[DK];
+  {
+    const int row = k_row_order(ln);
+    const int sw = k_swz<D>(row);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) roff[i] = row * ROWB + 16 * ((2 * i + hf) ^ sw);
+  }
+  uint32_t toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) toff[db][r] = bwd::tr_off<D>(lane, db, r);
+
+  f32x16 dkt[DB], dvt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
+  const float c = p.scale_log2;
+
+  auto tile = [&](int t, const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld)
+                  __attribute__((always_inline)) {
+    const int qt0 = t * BQt;
+    if (CAUSAL && qt0 + BQt - 1 < kw0) return;  // every query of the tile precedes this wave's keys
+    // S = Q K^T and dP = dO V^T (queries on MFMA rows, one key per lane)
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+      const u32x4 qa = *reinterpret_cast<const u32x4*>(lq + roff[i]);
+      const u32x4 ga = *reinterpret_cast<const u32x4*>(lg + roff[i]);
+      s = O_::mfma(qa, kf[i], s);
+      dp = O_::mfma(ga, vf[i], dp);
+    }
+    // element r is query qt0 + 16*(r>>3) + 8*hf + (r&7)
+    const bool masked = (qt0 + BQt > p.Nq) || (CAUSAL && qt0 < kw0 + 31);
+    u32x4 pp[PK], dsp[PK];
+#pragma unroll
+    for (int ks = 0; ks < PK; ++ks) {
+      const int qr = 16 * ks + 8 * hf;  // first query (tile row) of this lane's 8
+      const u32x4 l_lo = *reinterpret_cast<const u32x4*>(ll + qr);
+      const u32x4 l_hi = *reinterpret_cast<const u32x4*>(ll + qr + 4);
+      const u32x4 d_lo = *reinterpret_cast<const u32x4*>(ld + qr);
+      const u32x4 d_hi = *reinterpret_cast<const u32x4*>(ld + qr + 4);
+      float pv[8], dv8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t lb = u < 4 ? l_lo[u] : l_hi[u - 4];
+        const uint32_t dbits = u < 4 ? d_lo[u] : d_hi[u - 4];
+        const float lse2 = __builtin_bit_cast(float, lb) * bwd::kLog2e;
+        const float dl = __builtin_bit_cast(float, dbits);
+        const int r = 8 * ks + u;
+        float pr = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+        if (masked) {
+          const int q = qt0 + qr + u;
+          const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
+          pr = vis ? pr : 0.f;
+        }
+        pv[u] = pr;
+        dv8[u] = pr * (dp[r] - dl);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        pp[ks][tt] = O_::pack(pv[2 * tt], pv[2 * tt + 1]);
+        dsp[ks][tt] = O_::pack(dv8[2 * tt], dv8[2 * tt + 1]);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+    for (int ks = 0; ks < PK; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4 ga = bwd::tr_operand(lg + ks * 16 * ROWB, toff[db][0], toff[db][1]);
+        const u32x4 qa = bwd::tr_operand(lq + ks * 16 * ROWB, toff[db][0], toff[db][1]);
+        dvt[db] = O_::mfma(ga, pp[ks], dvt[db]);
+        dkt[db] = O_::mfma(qa, dsp[ks], dkt[db]);
+      }
+  };
+
+  // one barrier per tile, as in the dQ kernel
+  const int n_t = n_qtiles_all - t_begin;
+  if (n_t > 0) issue(t_begin, lds_q0, lds_g0, lds_l0, lds_d0);
+  for (int u = 0; u < n_t; ++u) {
+    const int t = t_begin + u;
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    bwd::bare_barrier();
+    const bool more = u + 1 < n_t;
+    if (u & 1) {
+      if (more) issue(t + 1, lds_q0, lds_g0, lds_l0, lds_d0);
+      tile(t, lds_q1, lds_g1, lds_l1, lds_d1);
+    } else {
+      if (more) issue(t + 1, lds_q1, lds_g1, lds_l1, lds_d1);
+      tile(t, lds_q0, lds_g0, lds_l0, lds_d0);
+    }
+  }
+
+  // dK = scale * dK^T, dV = dV^T (lane = key, registers = head-dim index)
+  if (my_k < p.Nk) {
+    uint16_t* krow = p.dk + kvo + (size_t)my_k * rs;
+    uint16_t* vrow = p.dv + kvo + (size_t)my_k * rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 wk, wv;
+        wk[0] = O_::pack(dkt[db][4 * a + 0] * p.scale, dkt[db][4 * a + 1] * p.scale);
+        wk[1] = O_::pack(dkt[db][4 * a + 2] * p.scale, dkt[db][4 * a + 3] * p.scale);
+        wv[0] = O_::pack(dvt[db][4 * a + 0], dvt[db][4 * a + 1]);
+        wv[1] = O_::pack(dvt[db][4 * a + 2], dvt[db][4 * a + 3]);
+        *reinterpret_cast<u32x2*>(krow + db * 32 + 8 * a + 4 * hf) = wk;
+        *reinterpret_cast<u32x2*>(vrow + db * 32 + 8 * a + 4 * hf) = wv;
+      }
+  }
+}
+
+}  // namespace mha

@@ -1,5 +1,5 @@
 /*
- * mha.h -- C ABI of the fused multi-head attention forward for AMD MI355X
+ * mha.h -- C ABI of the fused multi-head attention forward and backward for AMD MI355X
  * (gfx950 / CDNA4).
  *
  * The operation (per batch b and head h) is
@@ -83,6 +83,54 @@ typedef enum { MHA_DTYPE_FP16 = 0, MHA_DTYPE_BF16 = 1 } mha_dtype_t;
 mha_status_t mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int Nq, int Nk, int d, int causal, float scale,
                      void* stream, int dtype);
+
+/*
+ * mha_bwd -- attention backward: writes dQ, dK, dV and D.
+ *
+ * With P = exp(scale * Q K^T - LSE) (masked like the forward), regenerated
+ * tile by tile from the forward's LSE ("StreamKL", Methodology section 2),
+ * and D_i = sum_c dO_ic O_ic (the per-row term of the "SparkAttention"
+ * backward passage, there called dPsum, written as rowsum(dO o O)):
+ *
+ *     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q
+ *
+ * ("SparkAttention", backward passage: dV, dP, dS, dQ and dK per key block;
+ * the FlashAttention long-sequence post, "Attention parallelism": backward
+ * workers own blocks of keys). Keys no query sees (causal, key >= Nq) get
+ * dK = dV = 0.
+ *
+ * Arguments
+ *   q, o, dout  device pointers, [B, Nq, H, d], element type `dtype`: the
+ *               forward's inputs Q and output O, and dL/dO
+ *   k, v        device pointers, [B, Nk, H, d], element type `dtype`
+ *   lse         device pointer, [B, H, Nq] fp32: the forward's LSE (natural log)
+ *   dq          device pointer, [B, Nq, H, d], `dtype` (written)
+ *   dk, dv      device pointers, [B, Nk, H, d], `dtype` (written)
+ *   delta       device pointer, [B, H, Nq] fp32 (written: D, computed from
+ *               the o and dout given; the dQ and dK/dV kernels read it)
+ *   B, H, Nq, Nk, d, causal, scale, stream, dtype
+ *               as for mha_fwd, and equal to the forward's
+ * Each result element is the fp32 accumulation rounded to nearest even.
+ *
+ * Ownership and execution: as for mha_fwd. The library allocates nothing;
+ * `delta` is the caller's buffer for the one intermediate the kernels share.
+ * q, k, v, o, dout and lse are only read; dq, dk, dv and delta are
+ * overwritten entirely. The call enqueues three kernels on `stream` (D, then
+ * dQ, then dK/dV; only dK/dV when Nq == 0) and returns without
+ * synchronising.
+ *
+ * Requirements checked before anything is enqueued (violations return
+ * MHA_ERR_INVALID_ARG and write nothing): every pointer of a tensor with
+ * elements non-null; element-type pointers 16-byte aligned, fp32 pointers
+ * 4-byte aligned; dq, dk, dv and delta disjoint from each other and from
+ * every input; Nk >= 1 when B*H*Nq > 0. B*H == 0 (or Nq == Nk == 0) returns
+ * MHA_OK and enqueues nothing. Errors as for mha_fwd.
+ */
+mha_status_t mha_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                     float* delta, int B, int H, int Nq, int Nk, int d, int causal,
+                     float scale, void* stream, int dtype);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* mha_status_string(int status);

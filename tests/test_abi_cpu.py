@@ -115,3 +115,66 @@ def test_binding_has_no_fallback(tmp_path):
             _binding.load_library(str(tmp_path / "missing.so"))
     finally:
         _binding._lib = saved
+
+
+# ------------------------------------------------------------------ mha_bwd
+BQ, BK, BV, BO, BG, BL, DQ, DK, DV, DL = (0x10000000 * (i + 1) for i in range(10))
+GOOD_BWD = dict(q=BQ, k=BK, v=BV, o=BO, dout=BG, lse=BL, dq=DQ, dk=DK, dv=DV, delta=DL,
+                B=1, H=2, Nq=128, Nk=128, d=64, causal=0, scale=0.125, stream=None,
+                dtype=mha.MHA_DTYPE_BF16)
+
+
+def call_bwd(**kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    return mha.mha_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                       a["dv"], a["delta"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                       a["scale"], a["stream"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    *[(dict([(n, 0)]), mha.MHA_ERR_INVALID_ARG)
+      for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta")],
+    *[(dict([(n, GOOD_BWD[n] + 8)]), mha.MHA_ERR_INVALID_ARG)
+      for n in ("q", "k", "v", "o", "dout", "dq", "dk", "dv")],
+    (dict(lse=BL + 2), mha.MHA_ERR_INVALID_ARG),
+    (dict(delta=DL + 1), mha.MHA_ERR_INVALID_ARG),
+    (dict(B=-1), mha.MHA_ERR_INVALID_ARG),
+    (dict(Nq=-1), mha.MHA_ERR_INVALID_ARG),
+    (dict(Nk=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(d=96), mha.MHA_ERR_UNSUPPORTED),
+    (dict(causal=3), mha.MHA_ERR_INVALID_ARG),
+    (dict(dtype=5), mha.MHA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mha.MHA_ERR_INVALID_ARG),
+    (dict(scale=0.0), mha.MHA_ERR_INVALID_ARG),
+    (dict(dq=BQ), mha.MHA_ERR_INVALID_ARG),           # dq aliases q
+    (dict(dk=BG + 256), mha.MHA_ERR_INVALID_ARG),     # dk inside dout
+    (dict(dv=DK), mha.MHA_ERR_INVALID_ARG),           # two outputs alias
+    (dict(delta=DQ + 4096), mha.MHA_ERR_INVALID_ARG), # delta inside dq
+    (dict(delta=BL), mha.MHA_ERR_INVALID_ARG),        # delta aliases lse
+], ids=lambda x: str(x))
+def test_bwd_validation_rejects(lib, kw, want):
+    assert call_bwd(**kw) == want
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0, Nk=0),
+                                dict(B=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0,
+                                     delta=0)])
+def test_bwd_empty_problem_is_a_noop(lib, kw):
+    assert call_bwd(**kw) == mha.MHA_OK
+
+
+def test_bwd_no_queries_still_needs_key_buffers(lib):
+    # Nq == 0 with keys: dK = dV = 0 must be written, so their pointers are
+    # required while the query-side ones may be null
+    q_side = dict(q=0, o=0, dout=0, lse=0, dq=0, delta=0)
+    assert call_bwd(Nq=0, dk=0, **q_side) == mha.MHA_ERR_INVALID_ARG
+    assert call_bwd(Nq=0, v=0, **q_side) == mha.MHA_ERR_INVALID_ARG
+
+
+def test_bwd_no_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_bwd() == mha.MHA_ERR_DEVICE
+    assert call_bwd(Nq=0, q=0, o=0, dout=0, lse=0, dq=0, delta=0) == mha.MHA_ERR_DEVICE

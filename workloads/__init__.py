@@ -27,6 +27,10 @@ in the order Q, K, V, each of shape [B, N, H, d] in C order; rounded to fp16
 with numpy's round-to-nearest-even, or to bf16 with round-to-nearest-even on
 the fp32 bit pattern; for ``cross`` K is then multiplied by 2, which is exact
 in fp16.  The softmax scale is the fp32 value of 1/sqrt(d).
+
+The backward's output gradient dO of a workload is drawn the same way from
+``default_rng(seed + 1000)`` with the shape of Q ([B, Nq, H, d]) and rounded to
+the workload's type.
 """
 from __future__ import annotations
 
@@ -45,6 +49,8 @@ __all__ = [
     "round_bits",
     "make_inputs",
     "random_inputs",
+    "random_grad",
+    "make_grad",
 ]
 
 
@@ -165,3 +171,16 @@ def random_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: in
     if k_mult != 1.0:
         k = _double_bits(k, dtype, k_mult)
     return q, k, v
+
+
+def random_grad(B: int, H: int, Nq: int, d: int, dtype: str, seed: int) -> np.ndarray:
+    """iid N(0, 1) output gradient dO [B, Nq, H, d], rounded to ``dtype``."""
+    rng = np.random.default_rng(seed)
+    return round_bits(rng.standard_normal((B, Nq, H, d), dtype=np.float32), dtype)
+
+
+def make_grad(w: Workload | str) -> np.ndarray:
+    """dO of a named workload as uint16 bits of Q's shape (seed + 1000)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    return random_grad(w.B, w.H, w.Nq, w.d, w.dtype, w.seed + 1000)
