@@ -117,6 +117,22 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Scheduling pins for a run of TOTAL MFMAs that each consume R LDS reads:
+// the reads of the first AHEAD MFMAs, then for every MFMA n the MFMA and the
+// reads of MFMA n + AHEAD. Keeps few operands in flight (registers) while
+// the reads of later MFMAs overlap earlier ones.
+template <int N, int TOTAL, int R, int AHEAD>
+struct PinReads {
+  static __device__ __forceinline__ void apply() {
+    if constexpr (N == 0) __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);
+    if constexpr (N < TOTAL) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (N + AHEAD < TOTAL) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+      PinReads<N + 1, TOTAL, R, AHEAD>::apply();
+    }
+  }
+};
+
 // The 8 values of one transposed A operand.
 __device__ __forceinline__ u32x4 tr_operand(const uint8_t* base, uint32_t off0, uint32_t off1) {
   const u32x2 t0 = lds_read_tr16(base + off0);
@@ -168,7 +184,6 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
   constexpr int KB = BK / 32;            // 32-key blocks per tile
   constexpr int DK = D / 16;             // k-steps over the head dim
   constexpr int DB = D / 32;             // 32-row blocks of dQ^T
-  constexpr int PK = BK / 16;            // 16-key steps of dQ^T += K^T dS^T
   constexpr int CH = D / 8;              // 16-byte chunks per row
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BK * ROWB;
@@ -232,7 +247,9 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
   if (CAUSAL) n_kt = min(n_ktiles_all, (min(p.Nq, q0 + kBQ) + BK - 1) / BK);
   int jm = (p.Nk % BK) ? p.Nk / BK : n_ktiles_all;  // tiles [0, jm) need no mask
   if (CAUSAL) jm = min(jm, (qw0 + 1) / BK);
-  const int j_end = CAUSAL ? min(n_kt, qw0 / BK + 1) : n_kt;  // this wave's last tile + 1
+  int j_end = CAUSAL ? min(n_kt, qw0 / BK + 1) : n_kt;  // this wave's last tile + 1
+  if (qw0 >= p.Nq) j_end = 0;                               // no real rows in this wave
+  jm = min(jm, j_end);
 
   // K and V tiles: LDS copies, rows swizzled in 16-byte chunks by k_swz
   uint32_t c_off[NCPW];
@@ -274,73 +291,97 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
   const float c = p.scale_log2;
 
-  auto tile = [&](int j, const uint8_t* lk, const uint8_t* lv) __attribute__((always_inline)) {
-    if (j >= j_end) return;  // wave-uniform: past this wave's rows
-    // S^T = K Q^T and dP^T = V dO^T (keys on MFMA rows, one query per lane)
-    f32x16 s[KB], dp[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
-#pragma unroll
-    for (int i = 0; i < DK; ++i)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + roff[i] + kb * 32 * ROWB);
-        const u32x4 va = *reinterpret_cast<const u32x4*>(lv + roff[i] + kb * 32 * ROWB);
-        s[kb] = O_::mfma(ka, qf[i], s[kb]);
-        dp[kb] = O_::mfma(va, gf[i], dp[kb]);
-      }
-    // P = exp(scale*s - LSE), dS = P o (dP - D); element r of block kb is key
-    // j*BK + 32*kb + 16*(r>>3) + 8*hf + (r&7)
-    const int k0 = j * BK;
-    const bool masked = j >= jm;
-    u32x4 pf[PK];
+  // MASK: element masks (diagonal and tail tiles); a compile-time flag, so
+  // that each variant of the tile body is one straight-line block
+  // One 32-key block of a tile at a time, so that only one block's S^T and
+  // dP^T accumulators are live.
+  auto tile_body = [&](int j, const uint8_t* lk, const uint8_t* lv, auto mask_tag)
+                       __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T (keys on MFMA rows, one query per lane)
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < DK; ++i) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + roff[i] + kb * 32 * ROWB);
+        const u32x4 va = *reinterpret_cast<const u32x4*>(lv + roff[i] + kb * 32 * ROWB);
+        s = O_::mfma(ka, qf[i], s);
+        dp = O_::mfma(va, gf[i], dp);
+      }
+      bwd::PinReads<0, 2 * DK, 1, 4>::apply();
+      __builtin_amdgcn_sched_barrier(0);
+      // P = exp(scale*s - LSE), dS = P o (dP - D); element r is key
+      // j*BK + 32*kb + 16*(r>>3) + 8*hf + (r&7)
+      const int k0 = j * BK + kb * 32;
+      u32x4 pf[2];
       float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
-        if (masked) {
-          const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
+        float pv = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+        if constexpr (MASK) {
+          const int key = k0 + 16 * (r >> 3) + 8 * hf + (r & 7);
           const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
           pv = vis ? pv : 0.f;
         }
-        e[r] = pv * (dp[kb][r] - dlt);
+        e[r] = pv * (dp[r] - dlt);
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          pf[2 * kb + half][t] = O_::pack(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
+        for (int t = 0; t < 4; ++t) pf[half][t] = O_::pack(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      // dQ^T += K^T dS^T over this block's 32 keys
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 a = bwd::tr_operand(lk + (kb * 32 + ks * 16) * ROWB, toff[db][0], toff[db][1]);
+          dq[db] = O_::mfma(a, pf[ks], dq[db]);
+        }
+      bwd::PinReads<0, 2 * DB, 2, 4>::apply();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int ks = 0; ks < PK; ++ks)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4 a = bwd::tr_operand(lk + ks * 16 * ROWB, toff[db][0], toff[db][1]);
-        dq[db] = O_::mfma(a, pf[ks], dq[db]);
-      }
   };
-
   // One barrier per tile: tile j waits for its own copies (vmcnt) and for
   // this wave's LDS reads of tile j-1 (lgkmcnt); after the barrier every
-  // wave is done with tile j-1's buffers, which then take tile j+1.
-  issue(0, lds_k0, lds_v0);
-  for (int j = 0; j < n_kt; ++j) {
+  // wave is done with tile j-1's buffers, which then take tile j+1. Tile j
+  // lives in buffer j & 1. Tiles [0, jm) need no mask, [jm, j_end) need one,
+  // [j_end, n_kt) are past this wave's rows. Each kind of step is a
+  // straight-line body with the buffer parity fixed at compile time, so the
+  // accumulators stay in place across the loop.
+  auto step = [&](int j, auto par, auto mode) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    constexpr int MODE = decltype(mode)::value;  // 0 idle, 1 masked, 2 unmasked
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
     bwd::bare_barrier();
-    const bool more = j + 1 < n_kt;
-    if (j & 1) {
-      if (more) issue(j + 1, lds_k0, lds_v0);
-      tile(j, lds_k1, lds_v1);
-    } else {
-      if (more) issue(j + 1, lds_k1, lds_v1);
-      tile(j, lds_k0, lds_v0);
+    if (j + 1 < n_kt) {
+      if constexpr (P == 0) issue(j + 1, lds_k1, lds_v1);
+      else issue(j + 1, lds_k0, lds_v0);
     }
-  }
+    if constexpr (MODE != 0) {
+      using M = std::integral_constant<bool, MODE == 1>;
+      if constexpr (P == 0) tile_body(j, lds_k0, lds_v0, M{});
+      else tile_body(j, lds_k1, lds_v1, M{});
+    }
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  auto run = [&](int j0, int j1, auto mode) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) step(j++, Odd{}, mode);
+    for (; j + 1 < j1; j += 2) {
+      step(j, Even{}, mode);
+      step(j + 1, Odd{}, mode);
+    }
+    if (j < j1) step(j, Even{}, mode);
+  };
+  issue(0, lds_k0, lds_v0);
+  run(0, jm, std::integral_constant<int, 2>{});
+  run(jm, j_end, std::integral_constant<int, 1>{});
+  run(j_end, n_kt, std::integral_constant<int, 0>{});
 
   // dQ = scale * dQ^T, rounded to the I/O type
   if (my_q < p.Nq) {
@@ -476,10 +517,10 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
   const float c = p.scale_log2;
 
-  auto tile = [&](int t, const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld)
-                  __attribute__((always_inline)) {
+  auto tile_body = [&](int t, const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld,
+                       auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int qt0 = t * BQt;
-    if (CAUSAL && qt0 + BQt - 1 < kw0) return;  // every query of the tile precedes this wave's keys
     // S = Q K^T and dP = dO V^T (queries on MFMA rows, one key per lane)
     f32x16 s, dp;
 #pragma unroll
@@ -491,8 +532,9 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
       s = O_::mfma(qa, kf[i], s);
       dp = O_::mfma(ga, vf[i], dp);
     }
+    bwd::PinReads<0, 2 * DK, 1, 4>::apply();
+    __builtin_amdgcn_sched_barrier(0);
     // element r is query qt0 + 16*(r>>3) + 8*hf + (r&7)
-    const bool masked = (qt0 + BQt > p.Nq) || (CAUSAL && qt0 < kw0 + 31);
     u32x4 pp[PK], dsp[PK];
 #pragma unroll
     for (int ks = 0; ks < PK; ++ks) {
@@ -510,7 +552,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
         const float dl = __builtin_bit_cast(float, dbits);
         const int r = 8 * ks + u;
         float pr = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
-        if (masked) {
+        if constexpr (MASK) {
           const int q = qt0 + qr + u;
           const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
           pr = vis ? pr : 0.f;
@@ -524,6 +566,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
         dsp[ks][tt] = O_::pack(dv8[2 * tt], dv8[2 * tt + 1]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
     for (int ks = 0; ks < PK; ++ks)
@@ -534,24 +577,55 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
         dvt[db] = O_::mfma(ga, pp[ks], dvt[db]);
         dkt[db] = O_::mfma(qa, dsp[ks], dkt[db]);
       }
+    bwd::PinReads<0, 2 * PK * DB, 2, 4>::apply();
   };
-
-  // one barrier per tile, as in the dQ kernel
+  // Steps: one per query tile u = 0 .. n_t-1 (tile t_begin + u), each with
+  // one barrier; tile u lives in buffer u & 1. A causal wave has nothing to
+  // do for its first `f` tiles (all their queries precede its keys); tile f
+  // is its diagonal tile (the only one that needs an element mask, as
+  // BQt = 32 keys per wave); the rest are fully visible. Rows past Nq need
+  // no mask: their Q, dO, LSE and D are zero-filled, so P = 1 and dS = 0
+  // multiply zero rows. Each kind of step is a straight-line body with the
+  // buffer parity fixed at compile time, so the accumulators stay in place.
   const int n_t = n_qtiles_all - t_begin;
-  if (n_t > 0) issue(t_begin, lds_q0, lds_g0, lds_l0, lds_d0);
-  for (int u = 0; u < n_t; ++u) {
+  int f = CAUSAL ? min(n_t, wave) : 0;
+  if (kw0 >= p.Nk) f = n_t;  // no real keys in this wave
+  auto step = [&](int u, auto par, auto mode) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    constexpr int MODE = decltype(mode)::value;  // 0 idle, 1 masked, 2 unmasked
     const int t = t_begin + u;
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
     bwd::bare_barrier();
-    const bool more = u + 1 < n_t;
-    if (u & 1) {
-      if (more) issue(t + 1, lds_q0, lds_g0, lds_l0, lds_d0);
-      tile(t, lds_q1, lds_g1, lds_l1, lds_d1);
-    } else {
-      if (more) issue(t + 1, lds_q1, lds_g1, lds_l1, lds_d1);
-      tile(t, lds_q0, lds_g0, lds_l0, lds_d0);
+    if (u + 1 < n_t) {
+      if constexpr (P == 0) issue(t + 1, lds_q1, lds_g1, lds_l1, lds_d1);
+      else issue(t + 1, lds_q0, lds_g0, lds_l0, lds_d0);
+    }
+    if constexpr (MODE != 0) {
+      using M = std::integral_constant<bool, MODE == 1>;
+      if constexpr (P == 0) tile_body(t, lds_q0, lds_g0, lds_l0, lds_d0, M{});
+      else tile_body(t, lds_q1, lds_g1, lds_l1, lds_d1, M{});
+    }
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  auto run = [&](int u0, int u1, auto mode) __attribute__((always_inline)) {
+    int u = u0;
+    if (u < u1 && (u & 1)) step(u++, Odd{}, mode);
+    for (; u + 1 < u1; u += 2) {
+      step(u, Even{}, mode);
+      step(u + 1, Odd{}, mode);
+    }
+    if (u < u1) step(u, Even{}, mode);
+  };
+  if (n_t > 0) issue(t_begin, lds_q0, lds_g0, lds_l0, lds_d0);
+  run(0, f, std::integral_constant<int, 0>{});
+  if constexpr (CAUSAL) {
+    if (f < n_t) {
+      if (f & 1) step(f, Odd{}, std::integral_constant<int, 1>{});
+      else step(f, Even{}, std::integral_constant<int, 1>{});
     }
   }
+  run(f + (CAUSAL ? 1 : 0), n_t, std::integral_constant<int, 2>{});
 
   // dK = scale * dK^T, dV = dV^T (lane = key, registers = head-dim index)
   if (my_k < p.Nk) {
