@@ -1,4 +1,5 @@
-"""CPU fp64 oracle for the fused MHA forward and its backward.
+"""CPU fp64 oracle for the fused MHA forward, its split-over-keys form and its
+backward.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it; the product path must not.
@@ -14,3 +15,4 @@ from .attention import (  # noqa: F401
     log_sum_exp,
 )
 from .backward import attention_bwd, softmax_grad  # noqa: F401
+from .split import attention_fwd_split, merge_splits, split_partials  # noqa: F401
