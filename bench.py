@@ -32,13 +32,18 @@ METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak (B=1,H=8,N=16k,d=128 cau
 METRIC_BWD = ("attention bwd TFLOP/s (5-matmul count 10*B*H*Nq*Nk*d, halved causal) and % of "
               "MFMA bf16 peak")
 PEAK_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 MFMA peak
-KERNEL_SOURCES = [
-    os.path.join(ROOT, "head_attention_mha_amd", "csrc", "mha_fwd_kernel.hpp"),
-    os.path.join(ROOT, "head_attention_mha_amd", "csrc", "mha_api.hip"),
-]
-KERNEL_SOURCES_BWD = KERNEL_SOURCES + [
-    os.path.join(ROOT, "head_attention_mha_amd", "csrc", "mha_bwd_kernel.hpp"),
-]
+PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
+METRIC_SPLIT = ("attention decode forward (split over keys) HBM GB/s: Q, K, V read and O, LSE "
+                "written once, per second")
+_CSRC = os.path.join(ROOT, "head_attention_mha_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
+                  ("mha_common.hpp", "mha_fwd_kernel.hpp", "mha_fwd.hip")]
+KERNEL_SOURCES_SPLIT = [os.path.join(_CSRC, f) for f in
+                        ("mha_common.hpp", "mha_fwd_kernel.hpp", "mha_split_kernel.hpp",
+                         "mha_splitkv.hip")]
+KERNEL_SOURCES_BWD = [os.path.join(_CSRC, f) for f in
+                      ("mha_common.hpp", "mha_fwd_kernel.hpp", "mha_bwd_kernel.hpp",
+                       "mha_bwd.hip")]
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -56,7 +61,7 @@ def kernel_source_hash(sources=None) -> str:
 def hbm_traffic(workload: str, which: str = "fwd"):
     """Per-launch HBM bytes (FETCH + WRITE) from the committed counter summary,
     or None when there is none or the kernel sources changed since."""
-    name = f"hbm_traffic_{workload}.txt" if which == "fwd" else f"hbm_traffic_bwd_{workload}.txt"
+    name = f"hbm_traffic_{workload}.txt" if which == "fwd" else f"hbm_traffic_{which}_{workload}.txt"
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -65,7 +70,7 @@ def hbm_traffic(workload: str, which: str = "fwd"):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    srcs = KERNEL_SOURCES if which == "fwd" else KERNEL_SOURCES_BWD
+    srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT}[which]
     if fields.get("kernel_source_sha256_16") != kernel_source_hash(srcs):
         return None
     try:
@@ -110,6 +115,43 @@ def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float) -> dict:
         "sample": (f"{len(rows)} evenly spaced query rows of each of the {w.B * w.H} heads "
                    f"({len(rows) / w.Nq:.1%} of the rows, all their keys), fp64 NumPy, "
                    f"{t:.1f} s; FLOPs counted as 4*d*visible keys per row"),
+        "seconds": t,
+    }
+
+
+def cpu_baseline_split(w: wl.Workload, qb, kb, vb, target_s: float) -> dict:
+    """The fp64 split-over-keys oracle, as it stands, on whole batch entries
+    of the workload (all their heads), doubling their number until the run
+    takes about a quarter of ``target_s`` or covers the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
+                      if i.get("user_api") == "blas") or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    n_splits = max(1, min(256, -(-w.Nk // 2048)))
+    bounds = np.linspace(0, w.Nk, n_splits + 1).astype(np.int64)
+
+    def timed(nb):
+        q, k, v = (wl.bits_to_f64(x[:nb], w.dtype) for x in (qb, kb, vb))
+        t0 = time.perf_counter()
+        oracle.attention_fwd_split(q, k, v, w.causal, w.scale, bounds)
+        return time.perf_counter() - t0
+
+    nb = 1
+    t = timed(nb)
+    while nb < w.B and t < target_s / 4:
+        nb = min(w.B, 2 * nb)
+        t = timed(nb)
+    bytes_ = nb * w.H * ((2 * w.Nq + 2 * w.Nk) * w.d * 2 + 4 * w.Nq)
+    return {
+        "value": bytes_ / t / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"batch entries 0..{nb - 1} ({nb} of {w.B}, all {w.H} heads), {n_splits} key "
+                   f"splits, fp64 NumPy, {t:.2f} s; bytes counted as for the GPU line"),
         "seconds": t,
     }
 
@@ -164,8 +206,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="long_causal", choices=list(wl.WORKLOADS))
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
+    ap.add_argument("--workload", default=None,
+                    choices=list(wl.WORKLOADS) + list(wl.DECODE_WORKLOADS),
+                    help="default: long_causal (fwd, bwd), decode (splitkv)")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "splitkv"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -186,7 +230,8 @@ def main() -> int:
         print("bench.py: no GPU available", file=sys.stderr)
         return 1
     mha.load_library()
-    w = wl.WORKLOADS[args.workload]
+    name = args.workload or ("decode" if args.which == "splitkv" else "long_causal")
+    w = wl.WORKLOADS.get(name) or wl.DECODE_WORKLOADS[name]
     qb, kb, vb = wl.make_inputs(w)
     q, k, v = (to_device(torch, x, w.dtype) for x in (qb, kb, vb))
     o = torch.empty_like(q)
@@ -219,6 +264,20 @@ def main() -> int:
                 raise mha.MhaError(st, "mha_bwd")
 
         step = bwd_step
+    elif args.which == "splitkv":
+        n_splits = mha.mha_fwd_splitkv_splits(w.B, w.H, w.Nq, w.Nk)
+        o_part = torch.empty((n_splits, w.B, w.H, w.Nq, w.d), dtype=torch.float32, device=q.device)
+        lse_part = torch.empty((n_splits, w.B, w.H, w.Nq), dtype=torch.float32, device=q.device)
+        sargv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 w.B, w.H, w.Nq, w.Nk, w.d, int(w.causal), w.scale, n_splits,
+                 o_part.data_ptr(), lse_part.data_ptr(), sp, dt)
+
+        def split_step():
+            st = mha.mha_fwd_splitkv(*sargv)
+            if st != mha.MHA_OK:
+                raise mha.MhaError(st, "mha_fwd_splitkv")
+
+        step = split_step
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 2
@@ -249,15 +308,41 @@ def main() -> int:
     total_ms = ev[0].elapsed_time(ev[K])
     ms_per_step = total_ms / K
 
-    flops = w.flops if args.which == "fwd" else 2.5 * w.flops
+    flops = 2.5 * w.flops if args.which == "bwd" else w.flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (per.mean() * 1e-3) / 1e12
     traffic = hbm_traffic(w.name, args.which)
-    line = {
-        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
-        "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
+    srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT}
+    if args.which == "splitkv":
+        # HBM-bound: the metric is the algorithmic bytes moved per second
+        gbs = w.io_bytes / (ms_per_step * 1e-3) / 1e9
+        gbs_launch = w.io_bytes / (per.mean() * 1e-3) / 1e9
+        line = {
+            "metric": METRIC_SPLIT,
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
+            "tflops": round(tflops, 3),
+        }
+        roof = {"bound": "hbm", "achieved": round(gbs_launch, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs_launch / PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "mha_fwd_splitkv (partial and merge kernels, one call)",
+                "bytes_per_step": w.io_bytes, "n_splits": n_splits}
+    else:
+        line = {
+            "metric": METRIC if args.which == "fwd" else METRIC_BWD,
+            "value": round(tflops, 2),
+            "unit": "TFLOP/s",
+            "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
+        }
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": ("mha_fwd_kernel" if args.which == "fwd" else
+                           "mha_bwd (delta, dq and dkdv kernels, one call)")}
+    roof["launch_ms"] = {"mean": round(float(per.mean()), 5),
+                         "median": round(float(np.median(per)), 5),
+                         "min": round(float(per.min()), 5)}
+    line.update({
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -267,33 +352,23 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "pass": args.which, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "io_dtype": w.dtype, "accumulate": "fp32",
-                   "flops_per_step": flops},
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "kernel": ("mha_fwd_kernel" if args.which == "fwd" else
-                       "mha_bwd (delta, dq and dkdv kernels, one call)"),
-            "launch_ms": {"mean": round(float(per.mean()), 5), "median": round(float(np.median(per)), 5),
-                          "min": round(float(per.min()), 5)},
-        },
+        "config": {"workload": w.name, "pass": args.which, "B": w.B, "H": w.H, "Nq": w.Nq,
+                   "Nk": w.Nk, "d": w.d, "causal": w.causal, "io_dtype": w.dtype,
+                   "accumulate": "fp32", "flops_per_step": flops},
+        "roofline": roof,
         "timed_wall_s": round(wall, 3),
-        "kernel_source_sha256_16": kernel_source_hash(
-            KERNEL_SOURCES if args.which == "fwd" else KERNEL_SOURCES_BWD),
+        "kernel_source_sha256_16": kernel_source_hash(srcs[args.which]),
         "device": torch.cuda.get_device_name(0),
-    }
+    })
     if not args.no_cpu_baseline:
         print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
               flush=True)
         if args.which == "fwd":
             line["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
-        else:
+        elif args.which == "bwd":
             line["cpu_baseline"] = cpu_baseline_bwd(w, qb, kb, vb, gb, args.cpu_seconds)
+        else:
+            line["cpu_baseline"] = cpu_baseline_split(w, qb, kb, vb, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

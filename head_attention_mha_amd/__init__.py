@@ -16,9 +16,12 @@ from ._binding import (  # noqa: F401
     MhaError,
     attention,
     attention_backward,
+    attention_splitkv,
     load_library,
     mha_abi_version,
     mha_bwd,
+    mha_fwd_splitkv,
+    mha_fwd_splitkv_splits,
     mha_fwd,
     mha_status_string,
 )

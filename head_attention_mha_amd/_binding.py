@@ -26,7 +26,8 @@ MHA_DTYPE_FP16 = 0
 MHA_DTYPE_BF16 = 1
 
 # Every symbol include/mha.h declares.
-EXPORTED_SYMBOLS = ("mha_fwd", "mha_bwd", "mha_status_string", "mha_abi_version")
+EXPORTED_SYMBOLS = ("mha_fwd", "mha_fwd_splitkv", "mha_fwd_splitkv_splits", "mha_bwd",
+                    "mha_status_string", "mha_abi_version")
 
 _lib = None
 
@@ -53,6 +54,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
     ]
+    lib.mha_fwd_splitkv.restype = ctypes.c_int
+    lib.mha_fwd_splitkv.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int,
+    ]
+    lib.mha_fwd_splitkv_splits.restype = ctypes.c_int
+    lib.mha_fwd_splitkv_splits.argtypes = [ctypes.c_int] * 4
     lib.mha_bwd.restype = ctypes.c_int
     lib.mha_bwd.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -81,6 +91,50 @@ def mha_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, N
     """Call the C entry point with raw pointers; returns the status code."""
     return int(load_library().mha_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal),
                                       float(scale), stream, int(dtype)))
+
+
+def mha_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int, Nk: int,
+                    d: int, causal: int, scale: float, n_splits: int, o_part: int, lse_part: int,
+                    stream: int | None, dtype: int) -> int:
+    """Call the C entry point with raw pointers; returns the status code."""
+    return int(load_library().mha_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal),
+                                              float(scale), int(n_splits), o_part, lse_part,
+                                              stream, int(dtype)))
+
+
+def mha_fwd_splitkv_splits(B: int, H: int, Nq: int, Nk: int) -> int:
+    return int(load_library().mha_fwd_splitkv_splits(B, H, Nq, Nk))
+
+
+def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
+                      n_splits: int | None = None, stream=None):
+    """O, LSE = attention(Q, K, V) split over the keys (Nq <= 8, decoding).
+
+    Same tensors and results as ``attention``; the fp32 workspace for the
+    partial results is allocated with PyTorch. ``n_splits`` defaults to
+    ``mha_fwd_splitkv_splits``.
+    """
+    import torch
+
+    B, Nq, H, d, Nk = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = mha_fwd_splitkv_splits(B, H, Nq, Nk)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    o_part = torch.empty((n_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.empty((n_splits, B, H, Nq), dtype=torch.float32, device=q.device)
+    dt = MHA_DTYPE_BF16 if q.dtype == torch.bfloat16 else MHA_DTYPE_FP16
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = mha_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, Nq, Nk, d, int(bool(causal)), float(scale),
+                             n_splits, o_part.data_ptr(), lse_part.data_ptr(), stream, dt)
+    if st != MHA_OK:
+        raise MhaError(st, "mha_fwd_splitkv")
+    return out, lse
 
 
 def mha_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,

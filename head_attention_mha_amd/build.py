@@ -14,9 +14,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmha.so")
-SOURCES = [os.path.join(CSRC, "mha_api.hip")]
-DEPS = [os.path.join(CSRC, "mha_fwd_kernel.hpp"), os.path.join(CSRC, "mha_bwd_kernel.hpp"),
-        os.path.join(ROOT, "include", "mha.h")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("mha_api.hip", "mha_fwd.hip", "mha_splitkv.hip", "mha_bwd.hip")]
+DEPS = [os.path.join(CSRC, f) for f in
+        ("mha_common.hpp", "mha_fwd_kernel.hpp", "mha_split_kernel.hpp", "mha_bwd_kernel.hpp")]
+DEPS.append(os.path.join(ROOT, "include", "mha.h"))
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -24,6 +26,7 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
+    "-fvisibility=hidden",
     # Packed fp32 VALU ops stay off: plain scalar fp32 code only.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",

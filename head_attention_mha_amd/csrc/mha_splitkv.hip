@@ -1,0 +1,130 @@
+// C ABI of the split-over-keys forward: validation, template dispatch and
+// launch of the partial and merge kernels (contract in include/mha.h).
+#include "mha_common.hpp"
+#include "mha_split_kernel.hpp"
+
+using namespace mha_host;
+
+namespace {
+
+constexpr int kMaxSplits = 256;
+// Keys per split are a multiple of this (the partial kernel's block at d = 64).
+constexpr int kSplitAlign = 256;
+
+int split_len(int Nk, int n_splits) {
+  const long long per = ((long long)Nk + n_splits - 1) / n_splits;
+  return (int)(((per + kSplitAlign - 1) / kSplitAlign) * kSplitAlign);
+}
+
+// Host-side checks of an mha_fwd_splitkv call.
+mha_status_t validate_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                              int n_splits, float* o_part, float* lse_part, int dtype,
+                              bool* empty) {
+  bool e = false;
+  mha_status_t st = validate_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, 1, &e);
+  if (st != MHA_OK) return st;
+  if (n_splits < 1 || n_splits > kMaxSplits) return MHA_ERR_INVALID_ARG;
+  *empty = e;
+  if (e) return MHA_OK;
+  if (Nq > mha::split::kMaxNq) return MHA_ERR_UNSUPPORTED;
+  if ((long long)B * H * n_splits > 0x7fffffffLL || (long long)B * H * Nq > 0x7fffffffLL ||
+      (long long)Nk + kSplitAlign > 0x7fffffffLL)
+    return MHA_ERR_INVALID_ARG;
+  if (!o_part || !lse_part || !aligned(o_part, 16) || !aligned(lse_part, 4))
+    return MHA_ERR_INVALID_ARG;
+  const size_t es = 2;
+  const size_t nq = (size_t)B * Nq * H * d;
+  const size_t nk = (size_t)B * Nk * H * d;
+  const size_t nl = (size_t)B * H * Nq;
+  const size_t n_op = (size_t)n_splits * nl * d * 4, n_lp = (size_t)n_splits * nl * 4;
+  const void* bufs[5] = {q, k, v, o, lse};
+  const size_t sizes[5] = {nq * es, nk * es, nk * es, nq * es, nl * 4};
+  for (int i = 0; i < 5; ++i)
+    if (overlap(o_part, n_op, bufs[i], sizes[i]) || overlap(lse_part, n_lp, bufs[i], sizes[i]))
+      return MHA_ERR_INVALID_ARG;
+  if (overlap(o_part, n_op, lse_part, n_lp)) return MHA_ERR_INVALID_ARG;
+  return MHA_OK;
+}
+
+template <typename T, int D, int NQ, bool C>
+mha_status_t launch_split(const mha::SplitParams& p, hipStream_t stream) {
+  void* args[] = {const_cast<mha::SplitParams*>(&p)};
+  hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void*>(&mha::mha_split_partial_kernel<T, D, NQ, C>),
+      dim3(p.B * p.H * p.n_splits), dim3(mha::split::kThreads), args, 0, stream);
+  if (e == hipSuccess) {
+    const int rows = p.B * p.H * p.Nq;  // one workgroup per row
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&mha::mha_split_merge_kernel<T, D>),
+                        dim3(rows), dim3(mha::split::kThreads), args, 0, stream);
+  }
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MHA_ERR_LAUNCH;
+  }
+  return MHA_OK;
+}
+
+template <typename T, int D, bool C>
+mha_status_t dispatch_split_nq(const mha::SplitParams& p, hipStream_t s) {
+  if (p.Nq <= 1) return launch_split<T, D, 1, C>(p, s);
+  if (p.Nq <= 2) return launch_split<T, D, 2, C>(p, s);
+  if (p.Nq <= 4) return launch_split<T, D, 4, C>(p, s);
+  return launch_split<T, D, 8, C>(p, s);
+}
+
+template <typename T>
+mha_status_t dispatch_split(const mha::SplitParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 64) return causal ? dispatch_split_nq<T, 64, true>(p, s) : dispatch_split_nq<T, 64, false>(p, s);
+  return causal ? dispatch_split_nq<T, 128, true>(p, s) : dispatch_split_nq<T, 128, false>(p, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_fwd_splitkv_splits(int B, int H, int Nq, int Nk) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return 1;
+  // about 2048 workgroups in flight, each split at least one 256-key block
+  const long long bh = (long long)B * H;
+  long long n = (2048 + bh - 1) / bh;
+  const long long max_by_keys = ((long long)Nk + kSplitAlign - 1) / kSplitAlign;
+  if (n > max_by_keys) n = max_by_keys;
+  if (n > kMaxSplits) n = kMaxSplits;
+  return n < 1 ? 1 : (int)n;
+}
+
+mha_status_t mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                             int n_splits, float* o_part, float* lse_part, void* stream,
+                             int dtype) {
+  bool empty = false;
+  mha_status_t st = validate_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, n_splits,
+                                     o_part, lse_part, dtype, &empty);
+  if (st != MHA_OK || empty) return st;
+  st = check_device();
+  if (st != MHA_OK) return st;
+
+  mha::SplitParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.n_splits = n_splits;
+  p.split_len = split_len(Nk, n_splits);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MHA_DTYPE_BF16) return dispatch_split<mha::BF16>(p, d, causal != 0, s);
+  return dispatch_split<mha::F16>(p, d, causal != 0, s);
+}
+
+}  // extern "C"

@@ -1,6 +1,6 @@
 /*
- * mha.h -- C ABI of the fused multi-head attention forward and backward for AMD MI355X
- * (gfx950 / CDNA4).
+ * mha.h -- C ABI of the fused multi-head attention forward (whole, or split
+ * over the keys for decoding) and backward for AMD MI355X (gfx950 / CDNA4).
  *
  * The operation (per batch b and head h) is
  *
@@ -24,6 +24,13 @@
  */
 #ifndef MHA_MI355X_H
 #define MHA_MI355X_H
+
+/* Symbols the library exports (it is built with hidden default visibility). */
+#if defined(__GNUC__)
+#define MHA_API __attribute__((visibility("default")))
+#else
+#define MHA_API
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -80,9 +87,51 @@ typedef enum { MHA_DTYPE_FP16 = 0, MHA_DTYPE_BF16 = 1 } mha_dtype_t;
  * kernel (e.g. a pointer to too small a buffer) surfaces at the caller's next
  * synchronisation of `stream`.
  */
-mha_status_t mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int H, int Nq, int Nk, int d, int causal, float scale,
-                     void* stream, int dtype);
+MHA_API mha_status_t mha_fwd(const void* q, const void* k, const void* v, void* o,
+                             float* lse, int B, int H, int Nq, int Nk, int d, int causal,
+                             float scale, void* stream, int dtype);
+
+/*
+ * mha_fwd_splitkv -- the same forward (O and LSE, as mha_fwd) for few query
+ * rows, split over the keys: for decoding (one or a few new tokens per
+ * sequence against a long key/value cache).
+ *
+ * Workgroup (b, h, s) computes the softmax over the keys of split s,
+ * [s*L, (s+1)*L) with L = n_splits-th of Nk rounded up to 256 keys, giving a
+ * normalised partial O_s and its LSE_s per query row; a second kernel merges
+ * a row's splits with LSE = log sum_s exp(LSE_s) and
+ * O = sum_s exp(LSE_s - LSE) O_s ("StreamKL", Methodology section 3: keys
+ * split across thread blocks when NQ is small; the LSE as in its section 1).
+ * The result equals mha_fwd's up to rounding.
+ *
+ * Arguments: as for mha_fwd, plus
+ *   n_splits  number of key splits, 1 .. 256 (mha_fwd_splitkv_splits gives
+ *             a default); splits past the last key compute nothing
+ *   o_part    device pointer, fp32, n_splits*B*H*Nq*d elements, 16-byte
+ *             aligned: the caller's workspace for the partial outputs,
+ *             layout [n_splits, B, H, Nq, d] (overwritten)
+ *   lse_part  device pointer, fp32, n_splits*B*H*Nq elements, 4-byte
+ *             aligned: workspace for the partial LSEs, [n_splits, B, H, Nq]
+ *             (overwritten; -inf where a split has no visible key)
+ * Supported: Nq <= 8 (larger Nq returns MHA_ERR_UNSUPPORTED: use mha_fwd).
+ *
+ * Ownership and execution: as for mha_fwd; the library allocates nothing,
+ * the workspace belongs to the caller and may be reused once the enqueued
+ * work has completed (calls on one stream may share it). Two kernels are
+ * enqueued on `stream`. The workspace must not overlap any other argument
+ * (checked: MHA_ERR_INVALID_ARG). Other errors as for mha_fwd.
+ */
+MHA_API mha_status_t mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int B, int H, int Nq, int Nk, int d,
+                                     int causal, float scale, int n_splits, float* o_part,
+                                     float* lse_part, void* stream, int dtype);
+
+/*
+ * Suggested n_splits for mha_fwd_splitkv: enough splits for about 2048
+ * workgroups, each split at least 256 keys, at most 256 splits; 1 for
+ * invalid sizes. Pure host function.
+ */
+MHA_API int mha_fwd_splitkv_splits(int B, int H, int Nq, int Nk);
 
 /*
  * mha_bwd -- attention backward: writes dQ, dK, dV and D.
@@ -127,17 +176,17 @@ mha_status_t mha_fwd(const void* q, const void* k, const void* v, void* o, float
  * every input; Nk >= 1 when B*H*Nq > 0. B*H == 0 (or Nq == Nk == 0) returns
  * MHA_OK and enqueues nothing. Errors as for mha_fwd.
  */
-mha_status_t mha_bwd(const void* q, const void* k, const void* v, const void* o,
-                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                     float* delta, int B, int H, int Nq, int Nk, int d, int causal,
-                     float scale, void* stream, int dtype);
+MHA_API mha_status_t mha_bwd(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             float* delta, int B, int H, int Nq, int Nk, int d, int causal,
+                             float scale, void* stream, int dtype);
 
 /* Static, human-readable text for a status code (never NULL). */
-const char* mha_status_string(int status);
+MHA_API const char* mha_status_string(int status);
 
 /* ABI version of this header; bumped on any incompatible change. */
 #define MHA_ABI_VERSION 1
-int mha_abi_version(void);
+MHA_API int mha_abi_version(void);
 
 #ifdef __cplusplus
 }

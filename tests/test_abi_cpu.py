@@ -178,3 +178,57 @@ def test_bwd_no_device_reports_device_error(lib):
         pytest.skip("a GPU is present")
     assert call_bwd() == mha.MHA_ERR_DEVICE
     assert call_bwd(Nq=0, q=0, o=0, dout=0, lse=0, dq=0, delta=0) == mha.MHA_ERR_DEVICE
+
+
+# ---------------------------------------------------------- mha_fwd_splitkv
+OP, LP = 0x10000000 * 20, 0x10000000 * 21
+GOOD_SPLIT = dict(GOOD, Nq=4, n_splits=8, o_part=OP, lse_part=LP)
+
+
+def call_split(**kw):
+    a = dict(GOOD_SPLIT)
+    a.update(kw)
+    return mha.mha_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                               a["Nk"], a["d"], a["causal"], a["scale"], a["n_splits"],
+                               a["o_part"], a["lse_part"], a["stream"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(o_part=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(lse_part=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(o_part=OP + 4), mha.MHA_ERR_INVALID_ARG),     # o_part needs 16-byte alignment
+    (dict(lse_part=LP + 2), mha.MHA_ERR_INVALID_ARG),
+    (dict(n_splits=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(n_splits=257), mha.MHA_ERR_INVALID_ARG),
+    (dict(Nq=9), mha.MHA_ERR_UNSUPPORTED),
+    (dict(d=96), mha.MHA_ERR_UNSUPPORTED),
+    (dict(Nk=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(o_part=K + 64), mha.MHA_ERR_INVALID_ARG),     # workspace overlaps an input
+    (dict(lse_part=O), mha.MHA_ERR_INVALID_ARG),        # workspace overlaps the output
+    (dict(lse_part=OP + 64), mha.MHA_ERR_INVALID_ARG),  # the two workspaces overlap
+    (dict(scale=float("nan")), mha.MHA_ERR_INVALID_ARG),
+], ids=lambda x: str(x))
+def test_splitkv_validation_rejects(lib, kw, want):
+    assert call_split(**kw) == want
+
+
+def test_splitkv_empty_is_a_noop(lib):
+    assert call_split(Nq=0, o_part=0, lse_part=0) == mha.MHA_OK
+    assert call_split(B=0) == mha.MHA_OK
+
+
+def test_splitkv_default_splits(lib):
+    f = mha.mha_fwd_splitkv_splits
+    assert f(4, 32, 1, 32768) == 16          # 2048 workgroups over 128 heads
+    assert f(1, 1, 1, 100) == 1              # one 256-key block
+    assert f(1, 1, 1, 10 ** 6) == 256        # capped
+    assert f(64, 64, 1, 4096) == 1
+    assert f(0, 1, 1, 1) == 1 and f(1, 1, 1, 0) == 1
+
+
+def test_splitkv_no_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_split() == mha.MHA_ERR_DEVICE

@@ -28,6 +28,17 @@ with numpy's round-to-nearest-even, or to bf16 with round-to-nearest-even on
 the fp32 bit pattern; for ``cross`` K is then multiplied by 2, which is exact
 in fp16.  The softmax scale is the fp32 value of 1/sqrt(d).
 
+Decoding workloads (few new query rows against a long key/value cache, the
+small-NQ case "StreamKL" splits over keys, Methodology section 3; its
+contexts run from 4K to 512K tokens), drawn the same way:
+
+=============  ==  ==  ==  =====  ===  =====  ======  ====
+name           B   H   Nq  Nk     d    dtype  causal  seed
+=============  ==  ==  ==  =====  ===  =====  ======  ====
+decode         1   32  1   32768  128  bf16   no      5
+decode_multi   8   16  4   8192   64   fp16   no      6
+=============  ==  ==  ==  =====  ===  =====  ======  ====
+
 The backward's output gradient dO of a workload is drawn the same way from
 ``default_rng(seed + 1000)`` with the shape of Q ([B, Nq, H, d]) and rounded to
 the workload's type.
@@ -51,6 +62,7 @@ __all__ = [
     "random_inputs",
     "random_grad",
     "make_grad",
+    "DECODE_WORKLOADS",
 ]
 
 
@@ -101,13 +113,28 @@ WORKLOADS: dict[str, Workload] = {
 }
 
 
+DECODE_WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("decode", 1, 32, 1, 32768, 128, "bf16", False, 5),
+        Workload("decode_multi", 8, 16, 4, 8192, 64, "fp16", False, 6),
+    ]
+}
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bits.
 
     NaN inputs stay NaN (quiet bit forced)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb cannot wrap for non-NaN patterns (the largest, -inf,
+    # is 0xFF800000), so uint32 arithmetic is exact there
+    r = (u >> 16) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= 16
+    rounded = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         rounded[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
