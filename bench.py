@@ -33,6 +33,8 @@ METRIC_BWD = ("attention bwd TFLOP/s (5-matmul count 10*B*H*Nq*Nk*d, halved caus
               "MFMA bf16 peak")
 PEAK_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 MFMA peak
 PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
+METRIC_KL = ("attention KL(P1||P2) forward TFLOP/s (two QK^T products, 4*B*H*Nq*Nk*d, halved "
+             "causal) and % of MFMA bf16 peak")
 METRIC_SPLIT = ("attention decode forward (split over keys) HBM GB/s: Q, K, V read and O, LSE "
                 "written once, per second")
 _CSRC = os.path.join(ROOT, "head_attention_mha_amd", "csrc")
@@ -42,8 +44,11 @@ KERNEL_SOURCES_SPLIT = [os.path.join(_CSRC, f) for f in
                         ("mha_common.hpp", "mha_fwd_kernel.hpp", "mha_split_kernel.hpp",
                          "mha_splitkv.hip")]
 KERNEL_SOURCES_BWD = [os.path.join(_CSRC, f) for f in
-                      ("mha_common.hpp", "mha_fwd_kernel.hpp", "mha_bwd_kernel.hpp",
-                       "mha_bwd.hip")]
+                      ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp",
+                       "mha_bwd_kernel.hpp", "mha_bwd.hip")]
+KERNEL_SOURCES_KL = [os.path.join(_CSRC, f) for f in
+                     ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp", "mha_kl_kernel.hpp",
+                      "mha_kl.hip")]
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -70,7 +75,8 @@ def hbm_traffic(workload: str, which: str = "fwd"):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT}[which]
+    srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT,
+            "kl": KERNEL_SOURCES_KL}[which]
     if fields.get("kernel_source_sha256_16") != kernel_source_hash(srcs):
         return None
     try:
@@ -98,6 +104,42 @@ def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float) -> dict:
     def timed(rows):
         t0 = time.perf_counter()
         oracle.attention_fwd(q, k, v, w.causal, w.scale, rows=rows)
+        return time.perf_counter() - t0
+
+    pilot = np.unique(np.linspace(0, w.Nq - 1, 16).astype(np.int64))
+    t_p = max(timed(pilot), 1e-6)
+    n = int(min(w.Nq, max(16, len(pilot) * target_s / t_p)))
+    rows = np.unique(np.linspace(0, w.Nq - 1, n).astype(np.int64))
+    t = timed(rows)
+    vis = (rows + 1).clip(max=w.Nk) if w.causal else np.full(len(rows), w.Nk)
+    flops = 4.0 * w.d * float(vis.sum()) * w.B * w.H
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(rows)} evenly spaced query rows of each of the {w.B * w.H} heads "
+                   f"({len(rows) / w.Nq:.1%} of the rows, all their keys), fp64 NumPy, "
+                   f"{t:.1f} s; FLOPs counted as 4*d*visible keys per row"),
+        "seconds": t,
+    }
+
+
+def cpu_baseline_kl(w: wl.Workload, q1b, k1b, q2b, k2b, target_s: float) -> dict:
+    """The fp64 KL oracle, as it stands, on evenly spaced query rows of every
+    head (all keys), sized to about ``target_s``."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
+                      if i.get("user_api") == "blas") or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    x = [wl.bits_to_f64(a, w.dtype) for a in (q1b, k1b, q2b, k2b)]
+
+    def timed(rows):
+        t0 = time.perf_counter()
+        oracle.attention_kl(*x, w.causal, w.scale, rows=rows)
         return time.perf_counter() - t0
 
     pilot = np.unique(np.linspace(0, w.Nq - 1, 16).astype(np.int64))
@@ -207,9 +249,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    choices=list(wl.WORKLOADS) + list(wl.DECODE_WORKLOADS),
-                    help="default: long_causal (fwd, bwd), decode (splitkv)")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "splitkv"])
+                    choices=list(wl.WORKLOADS) + list(wl.DECODE_WORKLOADS) + list(wl.KL_WORKLOADS),
+                    help="default: long_causal (fwd, bwd), decode (splitkv), kl_long (kl)")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "splitkv", "kl"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -230,9 +272,13 @@ def main() -> int:
         print("bench.py: no GPU available", file=sys.stderr)
         return 1
     mha.load_library()
-    name = args.workload or ("decode" if args.which == "splitkv" else "long_causal")
-    w = wl.WORKLOADS.get(name) or wl.DECODE_WORKLOADS[name]
-    qb, kb, vb = wl.make_inputs(w)
+    name = args.workload or {"splitkv": "decode", "kl": "kl_long"}.get(args.which, "long_causal")
+    w = wl.WORKLOADS.get(name) or wl.DECODE_WORKLOADS.get(name) or wl.KL_WORKLOADS[name]
+    if args.which == "kl":
+        qb, kb, q2b, k2b = wl.make_kl_inputs(w)
+        vb = kb  # unused by the KL step
+    else:
+        qb, kb, vb = wl.make_inputs(w)
     q, k, v = (to_device(torch, x, w.dtype) for x in (qb, kb, vb))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=q.device)
@@ -278,6 +324,20 @@ def main() -> int:
                 raise mha.MhaError(st, "mha_fwd_splitkv")
 
         step = split_step
+    elif args.which == "kl":
+        q2, k2 = to_device(torch, q2b, w.dtype), to_device(torch, k2b, w.dtype)
+        kl_out = torch.empty_like(lse)
+        lse2 = torch.empty_like(lse)
+        kargv = (q.data_ptr(), k.data_ptr(), q2.data_ptr(), k2.data_ptr(), kl_out.data_ptr(),
+                 lse.data_ptr(), lse2.data_ptr(), w.B, w.H, w.Nq, w.Nk, w.d, int(w.causal),
+                 w.scale, sp, dt)
+
+        def kl_step():
+            st = mha.mha_kl_fwd(*kargv)
+            if st != mha.MHA_OK:
+                raise mha.MhaError(st, "mha_kl_fwd")
+
+        step = kl_step
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 2
@@ -312,7 +372,8 @@ def main() -> int:
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (per.mean() * 1e-3) / 1e12
     traffic = hbm_traffic(w.name, args.which)
-    srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT}
+    srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT,
+            "kl": KERNEL_SOURCES_KL}
     if args.which == "splitkv":
         # HBM-bound: the metric is the algorithmic bytes moved per second
         gbs = w.io_bytes / (ms_per_step * 1e-3) / 1e9
@@ -330,15 +391,15 @@ def main() -> int:
                 "bytes_per_step": w.io_bytes, "n_splits": n_splits}
     else:
         line = {
-            "metric": METRIC if args.which == "fwd" else METRIC_BWD,
+            "metric": {"fwd": METRIC, "bwd": METRIC_BWD, "kl": METRIC_KL}[args.which],
             "value": round(tflops, 2),
             "unit": "TFLOP/s",
             "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
         }
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
-                "kernel": ("mha_fwd_kernel" if args.which == "fwd" else
-                           "mha_bwd (delta, dq and dkdv kernels, one call)")}
+                "kernel": {"fwd": "mha_fwd_kernel", "kl": "mha_kl_kernel",
+                           "bwd": "mha_bwd (delta, dq and dkdv kernels, one call)"}[args.which]}
     roof["launch_ms"] = {"mean": round(float(per.mean()), 5),
                          "median": round(float(np.median(per)), 5),
                          "min": round(float(per.min()), 5)}
@@ -367,6 +428,8 @@ def main() -> int:
             line["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
         elif args.which == "bwd":
             line["cpu_baseline"] = cpu_baseline_bwd(w, qb, kb, vb, gb, args.cpu_seconds)
+        elif args.which == "kl":
+            line["cpu_baseline"] = cpu_baseline_kl(w, qb, kb, q2b, k2b, args.cpu_seconds)
         else:
             line["cpu_baseline"] = cpu_baseline_split(w, qb, kb, vb, args.cpu_seconds)
     else:

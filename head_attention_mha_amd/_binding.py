@@ -27,7 +27,7 @@ MHA_DTYPE_BF16 = 1
 
 # Every symbol include/mha.h declares.
 EXPORTED_SYMBOLS = ("mha_fwd", "mha_fwd_splitkv", "mha_fwd_splitkv_splits", "mha_bwd",
-                    "mha_status_string", "mha_abi_version")
+                    "mha_kl_fwd", "mha_status_string", "mha_abi_version")
 
 _lib = None
 
@@ -63,6 +63,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     ]
     lib.mha_fwd_splitkv_splits.restype = ctypes.c_int
     lib.mha_fwd_splitkv_splits.argtypes = [ctypes.c_int] * 4
+    lib.mha_kl_fwd.restype = ctypes.c_int
+    lib.mha_kl_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+    ]
     lib.mha_bwd.restype = ctypes.c_int
     lib.mha_bwd.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -135,6 +141,43 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     if st != MHA_OK:
         raise MhaError(st, "mha_fwd_splitkv")
     return out, lse
+
+
+def mha_kl_fwd(q1: int, k1: int, q2: int, k2: int, kl: int, lse1: int, lse2: int, B: int, H: int,
+               Nq: int, Nk: int, d: int, causal: int, scale: float, stream: int | None,
+               dtype: int) -> int:
+    """Call the C entry point with raw pointers; returns the status code."""
+    return int(load_library().mha_kl_fwd(q1, k1, q2, k2, kl, lse1, lse2, B, H, Nq, Nk, d,
+                                         int(causal), float(scale), stream, int(dtype)))
+
+
+def attention_kl(q1, k1, q2, k2, causal: bool = False, scale: float | None = None, stream=None):
+    """KL, LSE1, LSE2 = KL(softmax(Q1 K1^T) || softmax(Q2 K2^T)) per query row.
+
+    q1, q2: [B, Nq, H, d]; k1, k2: [B, Nk, H, d]; one dtype (float16 or
+    bfloat16), contiguous, on one HIP device. Returns three float32
+    [B, H, Nq] tensors. ``scale`` (both distributions) defaults to 1/sqrt(d).
+    """
+    import torch
+
+    B, Nq, H, d, Nk = _check_qkv(q1, k1, k1)
+    _check_qkv(q2, k2, k2)
+    if q2.shape != q1.shape or k2.shape != k1.shape or q2.dtype != q1.dtype or q2.device != q1.device:
+        raise ValueError("q2, k2 must match q1, k1 in shape, dtype and device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kl, lse1, lse2 = (torch.empty((B, H, Nq), dtype=torch.float32, device=q1.device)
+                      for _ in range(3))
+    dt = MHA_DTYPE_BF16 if q1.dtype == torch.bfloat16 else MHA_DTYPE_FP16
+    with torch.cuda.device(q1.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(q1.device).cuda_stream
+        st = mha_kl_fwd(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), kl.data_ptr(),
+                        lse1.data_ptr(), lse2.data_ptr(), B, H, Nq, Nk, d, int(bool(causal)),
+                        float(scale), stream, dt)
+    if st != MHA_OK:
+        raise MhaError(st, "mha_kl_fwd")
+    return kl, lse1, lse2
 
 
 def mha_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,

@@ -31,6 +31,7 @@
 #pragma once
 
 #include "mha_fwd_kernel.hpp"
+#include "mha_sync.hpp"
 
 namespace mha {
 
@@ -106,32 +107,6 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)((lds_u8*)lds_dst),
                                            4, voffset, 0, 0, 0);
 }
-
-// Workgroup barrier without a memory fence (a fenced barrier would also wait
-// for this wave's copy of the next tile). The waits that matter are explicit
-// before it; the empty asm statements keep the compiler from moving memory
-// accesses across it.
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Scheduling pins for a run of TOTAL MFMAs that each consume R LDS reads:
-// the reads of the first AHEAD MFMAs, then for every MFMA n the MFMA and the
-// reads of MFMA n + AHEAD. Keeps few operands in flight (registers) while
-// the reads of later MFMAs overlap earlier ones.
-template <int N, int TOTAL, int R, int AHEAD>
-struct PinReads {
-  static __device__ __forceinline__ void apply() {
-    if constexpr (N == 0) __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);
-    if constexpr (N < TOTAL) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (N + AHEAD < TOTAL) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-      PinReads<N + 1, TOTAL, R, AHEAD>::apply();
-    }
-  }
-};
 
 // The 8 values of one transposed A operand.
 __device__ __forceinline__ u32x4 tr_operand(const uint8_t* base, uint32_t off0, uint32_t off1) {
@@ -311,7 +286,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
         s = O_::mfma(ka, qf[i], s);
         dp = O_::mfma(va, gf[i], dp);
       }
-      bwd::PinReads<0, 2 * DK, 1, 4>::apply();
+      sync::PinReads<0, 2 * DK, 1, 4>::apply();
       __builtin_amdgcn_sched_barrier(0);
       // P = exp(scale*s - LSE), dS = P o (dP - D); element r is key
       // j*BK + 32*kb + 16*(r>>3) + 8*hf + (r&7)
@@ -341,7 +316,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
           const u32x4 a = bwd::tr_operand(lk + (kb * 32 + ks * 16) * ROWB, toff[db][0], toff[db][1]);
           dq[db] = O_::mfma(a, pf[ks], dq[db]);
         }
-      bwd::PinReads<0, 2 * DB, 2, 4>::apply();
+      sync::PinReads<0, 2 * DB, 2, 4>::apply();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -356,7 +331,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
     constexpr int P = decltype(par)::value;
     constexpr int MODE = decltype(mode)::value;  // 0 idle, 1 masked, 2 unmasked
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
-    bwd::bare_barrier();
+    sync::bare_barrier();
     if (j + 1 < n_kt) {
       if constexpr (P == 0) issue(j + 1, lds_k1, lds_v1);
       else issue(j + 1, lds_k0, lds_v0);
@@ -532,7 +507,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
       s = O_::mfma(qa, kf[i], s);
       dp = O_::mfma(ga, vf[i], dp);
     }
-    bwd::PinReads<0, 2 * DK, 1, 4>::apply();
+    sync::PinReads<0, 2 * DK, 1, 4>::apply();
     __builtin_amdgcn_sched_barrier(0);
     // element r is query qt0 + 16*(r>>3) + 8*hf + (r&7)
     u32x4 pp[PK], dsp[PK];
@@ -577,7 +552,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
         dvt[db] = O_::mfma(ga, pp[ks], dvt[db]);
         dkt[db] = O_::mfma(qa, dsp[ks], dkt[db]);
       }
-    bwd::PinReads<0, 2 * PK * DB, 2, 4>::apply();
+    sync::PinReads<0, 2 * PK * DB, 2, 4>::apply();
   };
   // Steps: one per query tile u = 0 .. n_t-1 (tile t_begin + u), each with
   // one barrier; tile u lives in buffer u & 1. A causal wave has nothing to
@@ -595,7 +570,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     constexpr int MODE = decltype(mode)::value;  // 0 idle, 1 masked, 2 unmasked
     const int t = t_begin + u;
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
-    bwd::bare_barrier();
+    sync::bare_barrier();
     if (u + 1 < n_t) {
       if constexpr (P == 0) issue(t + 1, lds_q1, lds_g1, lds_l1, lds_d1);
       else issue(t + 1, lds_q0, lds_g0, lds_l0, lds_d0);

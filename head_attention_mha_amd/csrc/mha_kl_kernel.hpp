@@ -1,0 +1,273 @@
+// Fused attention KL divergence ("StreamKL") for gfx950: per query row
+//
+//   KL_i = sum_j P1_ij (log P1_ij - log P2_ij),   P_t = softmax(scale Q_t K_t^T)
+//
+// in one pass over the keys, without materialising either Nq x Nk matrix
+// ("StreamKL", Methodology section 1). Each row keeps five running scalars:
+// the maxima m1, m2 of the two score rows, the sums l1, l2 of exp(S_t - m_t)
+// and acc = sum_j exp(S1_ij - m1)(S1_ij - S2_ij), all rescaled when a
+// maximum grows; at the end KL = acc / l1 + LSE2 - LSE1 with
+// LSE_t = m_t + log l_t. There is no P.V product: acc is one number per row,
+// not a row of an output matrix.
+//
+// Structure as the row-parallel kernels of this library: 4 waves per
+// workgroup, 32 query rows per wave with both rows' Q fragments held in
+// registers as MFMA B operands; tiles of 64 keys of K1 and K2 reach LDS by
+// buffer loads that write LDS directly, double-buffered, one barrier per
+// tile. S_t^T = K_t Q_t^T puts the query on the MFMA columns, so each lane
+// owns one query row (two lanes per row, one per half of the keys, merged
+// with a cross-half exchange). Causal tiles past the frontier are skipped
+// (the page's causal handling); only diagonal and tail tiles carry an element
+// mask. The softmax state lives in the exp2 domain (scores times
+// scale * log2(e)).
+#pragma once
+
+#include "mha_fwd_kernel.hpp"
+#include "mha_sync.hpp"
+
+namespace mha {
+
+struct KlParams {
+  const uint16_t* q1;
+  const uint16_t* k1;
+  const uint16_t* q2;
+  const uint16_t* k2;
+  float* kl;
+  float* lse1;
+  float* lse2;
+  int B, H, Nq, Nk;
+  float scale;       // softmax scale of both distributions (> 0)
+  float scale_log2;  // scale * log2(e)
+  int n_blocks;      // workgroups launched
+  int n_tiles;       // query blocks per (b, h)
+};
+
+namespace kl {
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBQ = 32 * kWaves;  // query rows per workgroup
+constexpr int kBK = 64;           // keys per tile
+constexpr float kLn2 = 0.69314718055994531f;
+}  // namespace kl
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
+  using O_ = Ops<T>;
+  constexpr int BK = kl::kBK;
+  constexpr int kBQ = kl::kBQ;
+  constexpr int NW = kl::kWaves;
+  constexpr int KB = BK / 32;            // 32-key blocks per tile
+  constexpr int DK = D / 16;             // k-steps over the head dim
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BK * ROWB;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int NCPW = TILEB / 1024 / NW;  // 1 KiB copies per wave per tensor
+  static_assert(NCPW >= 1 && (NW * RPI) % 16 == 0, "copy layout");
+  constexpr float NEG_INF = -__builtin_inff();
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[TILEB];  // K1, buffer 0
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[TILEB];  // K1, buffer 1
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[TILEB];  // K2, buffer 0
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[TILEB];  // K2, buffer 1
+
+  // work item: (batch, head, query block); a head's blocks on one XCD when
+  // the heads split evenly over the 8 XCDs, heaviest causal blocks first
+  const int lin = blockIdx.x;
+  const int BH = p.B * p.H;
+  const bool by_xcd = (BH & 7) == 0;
+  const int kk = by_xcd ? lin >> 3 : lin;
+  const int nh = by_xcd ? BH >> 3 : BH;
+  const int qi = kk / nh;
+  const int hh = kk - qi * nh;
+  const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;
+  const int qt = CAUSAL ? p.n_tiles - 1 - qi : qi;
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int q0 = qt * kBQ;
+
+  const size_t rs = (size_t)p.H * D;
+  const size_t qo = ((size_t)b * p.Nq * p.H + h) * D;
+  const size_t kvo = ((size_t)b * p.Nk * p.H + h) * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hf = lane >> 5;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + ln;
+
+  // Q1 and Q2 fragments of this lane's query row (B operands), read once
+  u32x4 q1f[DK], q2f[DK];
+  if (my_q < p.Nq) {
+    const uint16_t* r1 = p.q1 + qo + (size_t)my_q * rs + 8 * hf;
+    const uint16_t* r2 = p.q2 + qo + (size_t)my_q * rs + 8 * hf;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) {
+      q1f[i] = *reinterpret_cast<const u32x4*>(r1 + 16 * i);
+      q2f[i] = *reinterpret_cast<const u32x4*>(r2 + 16 * i);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DK; ++i) q1f[i] = q2f[i] = u32x4{0, 0, 0, 0};
+  }
+
+  // key tiles: [0, jm) need no mask, [jm, j_end) need one, [j_end, n_kt)
+  // are past this wave's rows
+  const int n_ktiles_all = (p.Nk + BK - 1) / BK;
+  int n_kt = n_ktiles_all;
+  if (CAUSAL) n_kt = min(n_ktiles_all, (min(p.Nq, q0 + kBQ) + BK - 1) / BK);
+  int jm = (p.Nk % BK) ? p.Nk / BK : n_ktiles_all;
+  if (CAUSAL) jm = min(jm, (qw0 + 1) / BK);
+  int j_end = CAUSAL ? min(n_kt, qw0 / BK + 1) : n_kt;
+  if (qw0 >= p.Nq) j_end = 0;
+  jm = min(jm, j_end);
+
+  uint32_t c_off[NCPW];
+#pragma unroll
+  for (int c = 0; c < NCPW; ++c) {
+    const int row = (c * NW + wave) * RPI + lane / CH;
+    c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ k_swz<D>(row));
+  }
+  auto issue = [&](int j, uint8_t* la, uint8_t* lb) __attribute__((always_inline)) {
+    const int nvalid = min(BK, p.Nk - j * BK);
+    const uint32_t bytes = (uint32_t)(nvalid - 1) * row_bytes + ROWB;
+    const auto r1 = make_rsrc(p.k1 + kvo + (size_t)j * BK * rs, bytes);
+    const auto r2 = make_rsrc(p.k2 + kvo + (size_t)j * BK * rs, bytes);
+#pragma unroll
+    for (int c = 0; c < NCPW; ++c) dma16(r1, la + (c * NW + wave) * 1024, c_off[c]);
+#pragma unroll
+    for (int c = 0; c < NCPW; ++c) dma16(r2, lb + (c * NW + wave) * 1024, c_off[c]);
+  };
+
+  uint32_t roff[DK];
+  {
+    const int key = k_row_order(ln);
+    const int sw = k_swz<D>(key);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) roff[i] = key * ROWB + 16 * ((2 * i + hf) ^ sw);
+  }
+
+  // running state of this lane's half of the row (m shared by both halves)
+  float m1 = NEG_INF, m2 = NEG_INF, l1 = 0.f, l2 = 0.f, acc = 0.f;
+  const float c = p.scale_log2;
+
+  // One 32-key block at a time (the online update runs per block), so that
+  // only one block's S1^T and S2^T accumulators are live.
+  auto tile_body = [&](int j, const uint8_t* la, const uint8_t* lb, auto mask_tag)
+                       __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      // S1^T = K1 Q1^T and S2^T = K2 Q2^T, keys on the MFMA rows
+      f32x16 s1, s2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s1[r] = s2[r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < DK; ++i) {
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + roff[i] + kb * 32 * ROWB);
+        const u32x4 a2 = *reinterpret_cast<const u32x4*>(lb + roff[i] + kb * 32 * ROWB);
+        s1 = O_::mfma(a1, q1f[i], s1);
+        s2 = O_::mfma(a2, q2f[i], s2);
+      }
+      sync::PinReads<0, 2 * DK, 1, 4>::apply();
+      __builtin_amdgcn_sched_barrier(0);
+      // scores in the exp2 domain; element r is key
+      // j*BK + 32*kb + 16*(r>>3) + 8*hf + (r&7)
+      float x1[16], x2[16];
+      float t1 = NEG_INF, t2 = NEG_INF;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float a = s1[r] * c, e = s2[r] * c;
+        if constexpr (MASK) {
+          const int key = j * BK + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
+          const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
+          a = vis ? a : NEG_INF;
+          e = vis ? e : NEG_INF;
+        }
+        x1[r] = a;
+        x2[r] = e;
+        t1 = fmaxf(t1, a);
+        t2 = fmaxf(t2, e);
+      }
+      // a row may see no key of this block (causal, diagonal tile): then
+      // its maximum stays as it was; the reference value 0 keeps the
+      // weights below at exp2(-inf) = 0 instead of exp2(-inf + inf)
+      const float n1 = fmaxf(m1, max_halves(t1));
+      const float n2 = fmaxf(m2, max_halves(t2));
+      const float r1 = n1 == NEG_INF ? 0.f : n1;
+      const float r2 = n2 == NEG_INF ? 0.f : n2;
+      const float al1 = fast_exp2(m1 - r1), al2 = fast_exp2(m2 - r2);
+      m1 = n1;
+      m2 = n2;
+      float sl1 = 0.f, sl2 = 0.f, sa = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p1 = fast_exp2(x1[r] - r1);
+        const float p2 = fast_exp2(x2[r] - r2);
+        // the difference of the raw scores, then scaled: finite also for
+        // masked keys (where p1 = 0), and exactly 0 where the two scores
+        // are equal (no fused multiply-add can mix their roundings)
+        const float dx = (s1[r] - s2[r]) * c;
+        sl1 += p1;
+        sl2 += p2;
+        sa = __builtin_fmaf(p1, dx, sa);
+      }
+      l1 = __builtin_fmaf(l1, al1, sl1);
+      l2 = __builtin_fmaf(l2, al2, sl2);
+      acc = __builtin_fmaf(acc, al1, sa);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto step = [&](int j, auto par, auto mode) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    constexpr int MODE = decltype(mode)::value;  // 0 idle, 1 masked, 2 unmasked
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    sync::bare_barrier();
+    if (j + 1 < n_kt) {
+      if constexpr (P == 0) issue(j + 1, lds_a1, lds_b1);
+      else issue(j + 1, lds_a0, lds_b0);
+    }
+    if constexpr (MODE != 0) {
+      using M = std::integral_constant<bool, MODE == 1>;
+      if constexpr (P == 0) tile_body(j, lds_a0, lds_b0, M{});
+      else tile_body(j, lds_a1, lds_b1, M{});
+    }
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  auto run = [&](int j0, int j1, auto mode) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) step(j++, Odd{}, mode);
+    for (; j + 1 < j1; j += 2) {
+      step(j, Even{}, mode);
+      step(j + 1, Odd{}, mode);
+    }
+    if (j < j1) step(j, Even{}, mode);
+  };
+  if (n_kt > 0) issue(0, lds_a0, lds_b0);
+  run(0, jm, std::integral_constant<int, 2>{});
+  run(jm, j_end, std::integral_constant<int, 1>{});
+  run(j_end, n_kt, std::integral_constant<int, 0>{});
+
+  // both halves of the row: add the sums, then KL = acc/l1 + LSE2 - LSE1
+  l1 = sum_halves(l1);
+  l2 = sum_halves(l2);
+  acc = sum_halves(acc);
+  if (hf == 0 && my_q < p.Nq) {
+    const float lse1 = (m1 + fast_log2(l1)) * kl::kLn2;
+    const float lse2 = (m2 + fast_log2(l2)) * kl::kLn2;
+    const size_t r = (size_t)bh * p.Nq + my_q;
+    p.lse1[r] = lse1;
+    p.lse2[r] = lse2;
+    // LSE2 - LSE1 from the differences of the maxima and of the log sums,
+    // not of the two LSEs (no cancellation of two large values, and exactly
+    // 0 for identical distributions)
+    const float dlse = (m2 - m1) + (fast_log2(l2) - fast_log2(l1));
+    p.kl[r] = (acc / l1 + dlse) * kl::kLn2;
+  }
+}
+
+}  // namespace mha

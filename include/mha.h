@@ -1,6 +1,7 @@
 /*
  * mha.h -- C ABI of the fused multi-head attention forward (whole, or split
- * over the keys for decoding) and backward for AMD MI355X (gfx950 / CDNA4).
+ * over the keys for decoding), its backward and the fused attention KL
+ * divergence, for AMD MI355X (gfx950 / CDNA4).
  *
  * The operation (per batch b and head h) is
  *
@@ -132,6 +133,37 @@ MHA_API mha_status_t mha_fwd_splitkv(const void* q, const void* k, const void* v
  * invalid sizes. Pure host function.
  */
 MHA_API int mha_fwd_splitkv_splits(int B, int H, int Nq, int Nk);
+
+/*
+ * mha_kl_fwd -- fused attention KL divergence: writes KL(P1 || P2) per query
+ * row and the two LSEs.
+ *
+ *     P_t = softmax(scale * Q_t K_t^T  [+ causal mask]),  t = 1, 2
+ *     KL_i = sum_j P1_ij (log P1_ij - log P2_ij)
+ *     LSE_t,i = ln( sum_j exp(scale * q_t,i . k_t,j) )  over the visible keys
+ *
+ * computed in one pass over the keys with five running scalars per row
+ * (m1, m2, l1, l2, acc) and KL = acc / l1 + LSE2 - LSE1, never writing either
+ * Nq x Nk matrix ("StreamKL", Methodology section 1; P1 is the fixed
+ * distribution of its standard distillation setting). LSE1 and LSE2 are what
+ * a backward would regenerate the distributions from (its section 2).
+ *
+ * Arguments
+ *   q1, q2      device pointers, [B, Nq, H, d], element type `dtype`
+ *   k1, k2      device pointers, [B, Nk, H, d], element type `dtype`
+ *   kl          device pointer, [B, H, Nq] fp32 (written; natural log units)
+ *   lse1, lse2  device pointers, [B, H, Nq] fp32 (written; natural log)
+ *   B, H, Nq, Nk, d, causal, scale, stream, dtype  as for mha_fwd (one scale
+ *               and one mask for both distributions)
+ *
+ * Ownership, execution and errors: as for mha_fwd (one kernel enqueued; the
+ * library allocates nothing; kl, lse1 and lse2 must not overlap each other
+ * or any input).
+ */
+MHA_API mha_status_t mha_kl_fwd(const void* q1, const void* k1, const void* q2,
+                                const void* k2, float* kl, float* lse1, float* lse2, int B,
+                                int H, int Nq, int Nk, int d, int causal, float scale,
+                                void* stream, int dtype);
 
 /*
  * mha_bwd -- attention backward: writes dQ, dK, dV and D.

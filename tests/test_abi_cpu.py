@@ -232,3 +232,45 @@ def test_splitkv_no_device_reports_device_error(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert call_split() == mha.MHA_ERR_DEVICE
+
+
+# --------------------------------------------------------------- mha_kl_fwd
+A1, A2, A3, A4, OK_, OL1, OL2 = (0x10000000 * (i + 30) for i in range(7))
+GOOD_KL = dict(q1=A1, k1=A2, q2=A3, k2=A4, kl=OK_, lse1=OL1, lse2=OL2, B=1, H=2, Nq=128,
+               Nk=128, d=128, causal=1, scale=0.088, stream=None, dtype=mha.MHA_DTYPE_BF16)
+
+
+def call_kl(**kw):
+    a = dict(GOOD_KL)
+    a.update(kw)
+    return mha.mha_kl_fwd(*(a[n] for n in ("q1", "k1", "q2", "k2", "kl", "lse1", "lse2", "B", "H",
+                                         "Nq", "Nk", "d", "causal", "scale", "stream", "dtype")))
+
+
+@pytest.mark.parametrize("kw,want", [
+    *[(dict([(n, 0)]), mha.MHA_ERR_INVALID_ARG)
+      for n in ("q1", "k1", "q2", "k2", "kl", "lse1", "lse2")],
+    *[(dict([(n, GOOD_KL[n] + 8)]), mha.MHA_ERR_INVALID_ARG) for n in ("q1", "k1", "q2", "k2")],
+    (dict(kl=OK_ + 2), mha.MHA_ERR_INVALID_ARG),
+    (dict(Nk=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(d=32), mha.MHA_ERR_UNSUPPORTED),
+    (dict(causal=5), mha.MHA_ERR_INVALID_ARG),
+    (dict(dtype=3), mha.MHA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), mha.MHA_ERR_INVALID_ARG),
+    (dict(kl=A2 + 64), mha.MHA_ERR_INVALID_ARG),   # output inside an input
+    (dict(lse2=OL1), mha.MHA_ERR_INVALID_ARG),     # two outputs alias
+], ids=lambda x: str(x))
+def test_kl_validation_rejects(lib, kw, want):
+    assert call_kl(**kw) == want
+
+
+def test_kl_empty_is_a_noop(lib):
+    assert call_kl(Nq=0, q1=0, q2=0, kl=0, lse1=0, lse2=0) == mha.MHA_OK
+    assert call_kl(H=0) == mha.MHA_OK
+
+
+def test_kl_no_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_kl() == mha.MHA_ERR_DEVICE

@@ -1,0 +1,170 @@
+"""Parity of the fused attention KL divergence (mha_kl_fwd, through the C ABI)
+with the fp64 oracle (oracle/kl.py), on the GPU.
+
+Bar: KL, LSE1 and LSE2 each within 1e-3 (max-abs) of the oracle, mean-abs of
+the KL error within 1e-4, every value finite. KL = acc/l1 + LSE2 - LSE1 is
+formed from the same fp32 row state as the LSEs, so the forward's LSE bar
+(1e-3) is applied to all three; the kernel's own error is far below it
+(scores accumulate exact 16-bit products in fp32).
+
+Also: identical distributions give KL = 0 and LSE1 = LSE2 exactly (the two
+score streams are the same bits), KL >= 0 up to the bar, LSE1 agrees with
+mha_fwd's LSE on the same Q1, K1, the results are deterministic, and
+unsupported head sizes raise.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+KL_MAX_ABS = 1e-3
+KL_MEAN_ABS = 1e-4
+LSE_MAX_ABS = 1e-3
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+@pytest.fixture(scope="module")
+def mha(torch_mod):
+    import head_attention_mha_amd as m
+    m.load_library()
+    return m
+
+
+def to_dev(torch, bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
+
+
+def run_kl(torch, mha, q1b, k1b, q2b, k2b, dtype, causal, scale):
+    """Raw mha_kl_fwd with NaN-prefilled outputs; returns numpy (KL, LSE1, LSE2)."""
+    q1, k1, q2, k2 = (to_dev(torch, x, dtype) for x in (q1b, k1b, q2b, k2b))
+    B, Nq, H, d = q1.shape
+    outs = [torch.full((B, H, Nq), float("nan"), dtype=torch.float32, device="cuda")
+            for _ in range(3)]
+    dt = mha.MHA_DTYPE_BF16 if dtype == "bf16" else mha.MHA_DTYPE_FP16
+    st = mha.mha_kl_fwd(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(),
+                        *(o.data_ptr() for o in outs), B, H, Nq, k1.shape[1], d, int(causal),
+                        scale, torch.cuda.current_stream().cuda_stream, dt)
+    assert st == mha.MHA_OK, mha.mha_status_string(st)
+    torch.cuda.synchronize()
+    return tuple(o.cpu().numpy().astype(np.float64) for o in outs)
+
+
+def check(torch, mha, q1b, k1b, q2b, k2b, dtype, causal, scale, rows=None, label=""):
+    kl, l1, l2 = run_kl(torch, mha, q1b, k1b, q2b, k2b, dtype, causal, scale)
+    for name, x in (("KL", kl), ("LSE1", l1), ("LSE2", l2)):
+        assert np.all(np.isfinite(x)), f"{label}: unwritten/non-finite {name}"
+    ref = oracle.attention_kl(*(wl.bits_to_f64(x, dtype) for x in (q1b, k1b, q2b, k2b)),
+                              causal, scale, rows=rows)
+    if rows is not None:
+        kl, l1, l2 = kl[:, :, rows], l1[:, :, rows], l2[:, :, rows]
+    e_kl, e1, e2 = (np.abs(a - b) for a, b in zip((kl, l1, l2), ref))
+    st = dict(kl_max=float(e_kl.max()), kl_mean=float(e_kl.mean()), lse1_max=float(e1.max()),
+              lse2_max=float(e2.max()), kl_ref_mean=float(ref[0].mean()), kl_min=float(kl.min()))
+    sys.__stderr__.write(f"[kl-parity] {label}: {st}\n")
+    assert st["kl_max"] <= KL_MAX_ABS, f"{label}: KL max-abs {st}"
+    assert st["kl_mean"] <= KL_MEAN_ABS, f"{label}: KL mean-abs {st}"
+    assert st["lse1_max"] <= LSE_MAX_ABS and st["lse2_max"] <= LSE_MAX_ABS, f"{label}: LSE {st}"
+    assert st["kl_min"] >= -KL_MAX_ABS, f"{label}: negative KL {st}"
+    return st, (kl, l1, l2)
+
+
+def _inputs(B, H, Nq, Nk, d, dtype, seed, noise=0.5):
+    w = wl.Workload("case", B, H, Nq, Nk, d, dtype, False, seed)
+    return wl.make_kl_inputs(w, noise)
+
+
+SHAPES = [
+    # B, H, Nq, Nk, d, dtype, causal
+    (1, 1, 1, 1, 64, "fp16", False),
+    (1, 1, 1, 1, 128, "bf16", True),
+    (2, 3, 77, 131, 64, "bf16", False),
+    (2, 3, 77, 131, 128, "fp16", True),
+    (1, 2, 131, 77, 64, "fp16", True),      # Nq > Nk, causal
+    (1, 2, 200, 1, 128, "bf16", False),     # a single key: KL = 0
+    (1, 2, 1, 300, 64, "bf16", False),      # a single query
+    (3, 1, 63, 65, 128, "bf16", True),
+    (1, 8, 300, 300, 128, "bf16", True),    # B*H = 8: XCD-grouped order
+    (2, 8, 257, 513, 64, "fp16", False),
+    (1, 1, 513, 1000, 128, "fp16", True),
+]
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=lambda c: "B{}H{}q{}k{}d{}{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], "c" if c[6] else ""))
+def test_kl_shapes(torch_mod, mha, case):
+    B, H, Nq, Nk, d, dtype, causal = case
+    q1, k1, q2, k2 = _inputs(B, H, Nq, Nk, d, dtype, 700 + Nq + Nk)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    check(torch_mod, mha, q1, k1, q2, k2, dtype, causal, scale, label=str(case))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_kl_far_apart(torch_mod, mha, dtype):
+    """Unrelated distributions with peaky rows (noise 3, scale 0.25): large KL."""
+    q1, k1, q2, k2 = _inputs(1, 2, 300, 700, 64, dtype, 71, noise=3.0)
+    check(torch_mod, mha, q1, k1, q2, k2, dtype, True, 0.25, label=f"far-{dtype}")
+
+
+@pytest.mark.parametrize("name", list(wl.KL_WORKLOADS))
+def test_kl_workloads(torch_mod, mha, name):
+    w = wl.KL_WORKLOADS[name]
+    q1, k1, q2, k2 = wl.make_kl_inputs(w)
+    rows = None
+    if w.Nq * w.Nk * w.B * w.H > 2 ** 31:
+        rng = np.random.default_rng(0)
+        rows = np.unique(np.concatenate([np.arange(40), np.arange(w.Nq - 16, w.Nq),
+                                         rng.choice(w.Nq, 150, replace=False)]))
+    check(torch_mod, mha, q1, k1, q2, k2, w.dtype, w.causal, w.scale, rows, name)
+
+
+def test_kl_identical_is_exactly_zero(torch_mod, mha):
+    q1, k1, _, _ = _inputs(2, 4, 200, 333, 128, "bf16", 72)
+    kl, l1, l2 = run_kl(torch_mod, mha, q1, k1, q1, k1, "bf16", True, 0.088)
+    assert np.all(kl == 0.0) and np.array_equal(l1, l2)
+
+
+def test_kl_lse_matches_forward(torch_mod, mha):
+    torch = torch_mod
+    q1, k1, q2, k2 = _inputs(1, 4, 300, 500, 128, "bf16", 73)
+    _, l1, _ = run_kl(torch, mha, q1, k1, q2, k2, "bf16", True, 0.088)
+    q, k = to_dev(torch, q1, "bf16"), to_dev(torch, k1, "bf16")
+    _, lse = mha.attention(q, k, k.clone(), causal=True, scale=0.088)
+    torch.cuda.synchronize()
+    assert np.abs(lse.cpu().numpy() - l1).max() <= 1e-4
+
+
+def test_kl_deterministic_and_binding(torch_mod, mha):
+    torch = torch_mod
+    q1b, k1b, q2b, k2b = _inputs(2, 8, 260, 260, 64, "fp16", 74)
+    a = run_kl(torch, mha, q1b, k1b, q2b, k2b, "fp16", False, 0.125)
+    b = run_kl(torch, mha, q1b, k1b, q2b, k2b, "fp16", False, 0.125)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    t = [to_dev(torch, x, "fp16") for x in (q1b, k1b, q2b, k2b)]
+    kl, l1, l2 = mha.attention_kl(*t, causal=False, scale=0.125)
+    torch.cuda.synchronize()
+    assert np.array_equal(kl.cpu().numpy().astype(np.float64), a[0])
+    q96 = torch.zeros((1, 8, 1, 96), dtype=torch.float16, device="cuda")
+    with pytest.raises(mha.MhaError) as e:
+        mha.attention_kl(q96, q96.clone(), q96.clone(), q96.clone())
+    assert e.value.status == mha.MHA_ERR_UNSUPPORTED

@@ -39,6 +39,23 @@ decode         1   32  1   32768  128  bf16   no      5
 decode_multi   8   16  4   8192   64   fp16   no      6
 =============  ==  ==  ==  =====  ===  =====  ======  ====
 
+Attention-KL workloads (two distributions over the same keys: a fixed one
+from Q1, K1 and one to be trained towards it from Q2, K2; "StreamKL" uses
+4K-512K contexts, 32 heads, bf16):
+
+=========  ==  ==  =====  =====  ===  =====  ======  ====
+name       B   H   Nq     Nk     d    dtype  causal  seed
+=========  ==  ==  =====  =====  ===  =====  ======  ====
+kl_long    1   8   16384  16384  128  bf16   yes     7
+kl_mid     2   16  4096   4096   64   fp16   no      8
+=========  ==  ==  =====  =====  ===  =====  ======  ====
+
+Recipe: from ``default_rng(seed)`` draw N1 (shape of Q), N2 (shape of K), N3
+(shape of Q), N4 (shape of K) in that order (standard normal, float32); Q1 and
+K1 are N1 and N2 rounded to the type; Q2 and K2 are Q1 + N3/2 and K1 + N4/2
+computed in float32 from the rounded Q1, K1 and rounded to the type (a
+perturbed copy, as a student near its teacher).
+
 The backward's output gradient dO of a workload is drawn the same way from
 ``default_rng(seed + 1000)`` with the shape of Q ([B, Nq, H, d]) and rounded to
 the workload's type.
@@ -63,6 +80,8 @@ __all__ = [
     "random_grad",
     "make_grad",
     "DECODE_WORKLOADS",
+    "KL_WORKLOADS",
+    "make_kl_inputs",
 ]
 
 
@@ -118,6 +137,15 @@ DECODE_WORKLOADS: dict[str, Workload] = {
     for w in [
         Workload("decode", 1, 32, 1, 32768, 128, "bf16", False, 5),
         Workload("decode_multi", 8, 16, 4, 8192, 64, "fp16", False, 6),
+    ]
+}
+
+
+KL_WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("kl_long", 1, 8, 16384, 16384, 128, "bf16", True, 7),
+        Workload("kl_mid", 2, 16, 4096, 4096, 64, "fp16", False, 8),
     ]
 }
 
@@ -211,3 +239,18 @@ def make_grad(w: Workload | str) -> np.ndarray:
     if isinstance(w, str):
         w = WORKLOADS[w]
     return random_grad(w.B, w.H, w.Nq, w.d, w.dtype, w.seed + 1000)
+
+
+def make_kl_inputs(w: Workload | str, noise: float = 0.5):
+    """Q1, K1, Q2, K2 of an attention-KL workload as uint16 bits."""
+    if isinstance(w, str):
+        w = KL_WORKLOADS[w]
+    rng = np.random.default_rng(w.seed)
+    qs, ks = (w.B, w.Nq, w.H, w.d), (w.B, w.Nk, w.H, w.d)
+    q1 = round_bits(rng.standard_normal(qs, dtype=np.float32), w.dtype)
+    k1 = round_bits(rng.standard_normal(ks, dtype=np.float32), w.dtype)
+    n3 = rng.standard_normal(qs, dtype=np.float32)
+    n4 = rng.standard_normal(ks, dtype=np.float32)
+    q2 = round_bits(bits_to_f32(q1, w.dtype) + np.float32(noise) * n3, w.dtype)
+    k2 = round_bits(bits_to_f32(k1, w.dtype) + np.float32(noise) * n4, w.dtype)
+    return q1, k1, q2, k2
