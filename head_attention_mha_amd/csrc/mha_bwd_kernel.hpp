@@ -74,10 +74,27 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* ptr) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// 16-byte-chunk swizzle of the tiles that are read both as MFMA rows (16
+// lanes read the 16 rows k_row_order(0..15) at one chunk) and by transpose
+// reads (16 lanes read 4 consecutive rows x 2 chunks, 32 lanes 4 rows x 4
+// chunks). With t = row & 3 and m = (row >> 2) & 3, the 16 rows of a row
+// read get 16 (d = 128) or, per row parity, 8 (d = 64) different chunk
+// positions, and the 4 rows of a transpose read put their chunks on
+// disjoint positions, whether the LDS serves 128 or 256 bytes per pass.
+// (The forward's swizzle, made for row reads only, gives 4-way conflicts on
+// the transpose reads.)
+template <int D>
+__device__ __forceinline__ int t_swz(int row) {
+  const int t = row & 3, m = (row >> 2) & 3;
+  const int gray = m ^ (m >> 1);
+  if constexpr (D == 128) return (4 * t + 2 * (t >> 1)) ^ gray;  // 16 chunks per row
+  else return (2 * t) ^ gray;                                    // 8 chunks per row
+}
+
 // Per-lane byte offsets of the transpose reads that form the A operand
 // "rows = head-dim index 32*db + (lane % 32), k-slots = 8 consecutive tile
 // rows 16*ks + 8*(lane / 32) + 0..7" from a row-major tile whose 16-byte
-// chunks are swizzled by k_swz<D> of the row: two reads per operand, the
+// chunks are swizzled by t_swz<D> of the row: two reads per operand, the
 // second 4 rows further (r = 0, 1). Lane (g, a) of 16-lane group g supplies
 // the 8-byte piece of row 8*(g/2) + 4r + a/4 at head-dim index
 // 32*db + 16*(g%2) + 4*(a%4). Everything but these offsets (the 16-row step
@@ -88,7 +105,7 @@ __device__ __forceinline__ uint32_t tr_off(int lane, int db, int r) {
   const int g = lane >> 4, a = lane & 15;
   const int row = 8 * (g >> 1) + 4 * r + (a >> 2);
   const int chunk = 4 * db + 2 * (g & 1) + ((a & 3) >> 1);
-  return row * ROWB + 16 * (chunk ^ k_swz<D>(row)) + 8 * (a & 1);
+  return row * ROWB + 16 * (chunk ^ t_swz<D>(row)) + 8 * (a & 1);
 }
 
 // Two packed 16-bit values -> fp32.
@@ -226,12 +243,12 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
   if (qw0 >= p.Nq) j_end = 0;                               // no real rows in this wave
   jm = min(jm, j_end);
 
-  // K and V tiles: LDS copies, rows swizzled in 16-byte chunks by k_swz
+  // K and V tiles: LDS copies, rows swizzled in 16-byte chunks by t_swz
   uint32_t c_off[NCPW];
 #pragma unroll
   for (int c = 0; c < NCPW; ++c) {
     const int row = (c * NW + wave) * RPI + lane / CH;
-    c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ k_swz<D>(row));
+    c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ bwd::t_swz<D>(row));
   }
   auto issue = [&](int j, uint8_t* lk, uint8_t* lv) __attribute__((always_inline)) {
     const int nvalid = min(BK, p.Nk - j * BK);
@@ -249,7 +266,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
   uint32_t roff[DK];
   {
     const int key = k_row_order(ln);
-    const int sw = k_swz<D>(key);
+    const int sw = bwd::t_swz<D>(key);
 #pragma unroll
     for (int i = 0; i < DK; ++i) roff[i] = key * ROWB + 16 * ((2 * i + hf) ^ sw);
   }
@@ -450,7 +467,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
 #pragma unroll
   for (int c = 0; c < NCPW; ++c) {
     const int row = (c * NW + wave) * RPI + lane / CH;
-    c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ k_swz<D>(row));
+    c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ bwd::t_swz<D>(row));
   }
   // copies per wave per tile: NCPW each of Q and dO, plus LSE on wave 0 and
   // D on wave 1
@@ -475,7 +492,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   uint32_t roff[DK];
   {
     const int row = k_row_order(ln);
-    const int sw = k_swz<D>(row);
+    const int sw = bwd::t_swz<D>(row);
 #pragma unroll
     for (int i = 0; i < DK; ++i) roff[i] = row * ROWB + 16 * ((2 * i + hf) ^ sw);
   }
