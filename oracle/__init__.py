@@ -1,5 +1,5 @@
 """CPU fp64 oracle for the fused MHA forward, its split-over-keys form, its
-backward and the attention KL divergence.
+backward, the attention KL divergence and the output projection.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it; the product path must not.
@@ -17,3 +17,4 @@ from .attention import (  # noqa: F401
 from .backward import attention_bwd, softmax_grad  # noqa: F401
 from .split import attention_fwd_split, merge_splits, split_partials  # noqa: F401
 from .kl import attention_kl, kl_online_terms  # noqa: F401
+from .proj import out_proj, out_proj_bruteforce, out_proj_by_heads  # noqa: F401
