@@ -35,6 +35,8 @@ PEAK_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 MFMA peak
 PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
 METRIC_KL = ("attention KL(P1||P2) forward TFLOP/s (two QK^T products, 4*B*H*Nq*Nk*d, halved "
              "causal) and % of MFMA bf16 peak")
+METRIC_PROJ = ("output projection (head concat then O W^T + b) TFLOP/s, 2*B*Nq*H*d*E, and % of "
+               "MFMA bf16 peak")
 METRIC_SPLIT = ("attention decode forward (split over keys) HBM GB/s: Q, K, V read and O, LSE "
                 "written once, per second")
 _CSRC = os.path.join(ROOT, "head_attention_mha_amd", "csrc")
@@ -46,6 +48,9 @@ KERNEL_SOURCES_SPLIT = [os.path.join(_CSRC, f) for f in
 KERNEL_SOURCES_BWD = [os.path.join(_CSRC, f) for f in
                       ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp",
                        "mha_bwd_kernel.hpp", "mha_bwd.hip")]
+KERNEL_SOURCES_PROJ = [os.path.join(_CSRC, f) for f in
+                       ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp",
+                        "mha_proj_kernel.hpp", "mha_proj.hip")]
 KERNEL_SOURCES_KL = [os.path.join(_CSRC, f) for f in
                      ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp", "mha_kl_kernel.hpp",
                       "mha_kl.hip")]
@@ -76,7 +81,7 @@ def hbm_traffic(workload: str, which: str = "fwd"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT,
-            "kl": KERNEL_SOURCES_KL}[which]
+            "kl": KERNEL_SOURCES_KL, "proj": KERNEL_SOURCES_PROJ}[which]
     if fields.get("kernel_source_sha256_16") != kernel_source_hash(srcs):
         return None
     try:
@@ -243,15 +248,105 @@ def cpu_baseline_bwd(w: wl.Workload, qb, kb, vb, gb, target_s: float) -> dict:
     }
 
 
+def bench_proj(args, torch, mha, w) -> int:
+    """The output-projection pass (its own workload type: O, W, bias)."""
+    ob, wb, bb = wl.make_proj_inputs(w)
+    o, wt, b = (to_device(torch, x, w.dtype) for x in (ob, wb, bb))
+    y = torch.empty((w.B, w.Nq, w.E), dtype=o.dtype, device=o.device)
+    stream = torch.cuda.current_stream()
+    dt = mha.MHA_DTYPE_BF16 if w.dtype == "bf16" else mha.MHA_DTYPE_FP16
+    argv = (o.data_ptr(), wt.data_ptr(), b.data_ptr(), y.data_ptr(), w.B, w.Nq, w.H, w.d, w.E,
+            stream.cuda_stream, dt)
+
+    def step():
+        st = mha.mha_out_proj(*argv)
+        if st != mha.MHA_OK:
+            raise mha.MhaError(st, "mha_out_proj")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
+    ms = ev[0].elapsed_time(ev[K]) / K
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    achieved = w.flops / (per.mean() * 1e-3) / 1e12
+    line = {
+        "metric": METRIC_PROJ, "value": round(tflops, 2), "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2), "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "pass": "proj", "B": w.B, "Nq": w.Nq, "H": w.H, "d": w.d,
+                   "E": w.E, "io_dtype": w.dtype, "accumulate": "fp32", "flops_per_step": w.flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": hbm_traffic(w.name, "proj"), "kernel": "mha_proj_kernel",
+                     "launch_ms": {"mean": round(float(per.mean()), 5),
+                                   "median": round(float(np.median(per)), 5),
+                                   "min": round(float(per.min()), 5)}},
+        "timed_wall_s": round(wall, 3),
+        "kernel_source_sha256_16": kernel_source_hash(KERNEL_SOURCES_PROJ),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
+              flush=True)
+        line["cpu_baseline"] = cpu_baseline_proj(w, ob, wb, bb, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline_proj(w, ob, wb, bb, target_s: float) -> dict:
+    """The fp64 projection oracle, as it stands, on leading token rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
+                      if i.get("user_api") == "blas") or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    wt, b = wl.bits_to_f64(wb, w.dtype), wl.bits_to_f64(bb, w.dtype)
+    x = ob.reshape(w.B * w.Nq, w.H, w.d)
+
+    def timed(n):
+        o = wl.bits_to_f64(x[:n], w.dtype)[None]
+        t0 = time.perf_counter()
+        oracle.out_proj(o, wt, b)
+        return time.perf_counter() - t0
+
+    n = min(w.B * w.Nq, 256)
+    t = timed(n)
+    while n < w.B * w.Nq and t < target_s / 4:
+        n = min(w.B * w.Nq, 2 * n)
+        t = timed(n)
+    flops = 2.0 * n * w.H * w.d * w.E
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"the first {n} of {w.B * w.Nq} token rows, fp64 NumPy matmul, {t:.2f} s"),
+            "seconds": t}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    choices=list(wl.WORKLOADS) + list(wl.DECODE_WORKLOADS) + list(wl.KL_WORKLOADS),
-                    help="default: long_causal (fwd, bwd), decode (splitkv), kl_long (kl)")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "splitkv", "kl"])
+                    choices=(list(wl.WORKLOADS) + list(wl.DECODE_WORKLOADS) + list(wl.KL_WORKLOADS)
+                             + list(wl.PROJ_WORKLOADS)),
+                    help="default: long_causal (fwd, bwd), decode (splitkv), kl_long (kl), "
+                         "proj_long (proj)")
+    ap.add_argument("--pass", dest="which", default="fwd",
+                    choices=["fwd", "bwd", "splitkv", "kl", "proj"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -272,7 +367,10 @@ def main() -> int:
         print("bench.py: no GPU available", file=sys.stderr)
         return 1
     mha.load_library()
-    name = args.workload or {"splitkv": "decode", "kl": "kl_long"}.get(args.which, "long_causal")
+    name = args.workload or {"splitkv": "decode", "kl": "kl_long",
+                             "proj": "proj_long"}.get(args.which, "long_causal")
+    if args.which == "proj":
+        return bench_proj(args, torch, mha, wl.PROJ_WORKLOADS[name])
     w = wl.WORKLOADS.get(name) or wl.DECODE_WORKLOADS.get(name) or wl.KL_WORKLOADS[name]
     if args.which == "kl":
         qb, kb, q2b, k2b = wl.make_kl_inputs(w)

@@ -1,5 +1,5 @@
-"""Fused multi-head attention (forward, split-KV decode, backward) and attention
-KL divergence for AMD MI355X (gfx950).
+"""Fused multi-head attention (forward, split-KV decode, backward), attention
+KL divergence and the output projection, for AMD MI355X (gfx950).
 
 The computation lives in the HIP library ``libmha.so`` behind the C ABI of
 include/mha.h; this package only binds it (see ``_binding``).
@@ -20,9 +20,11 @@ from ._binding import (  # noqa: F401
     attention_kl,
     attention_splitkv,
     load_library,
+    out_proj,
     mha_abi_version,
     mha_bwd,
     mha_kl_fwd,
+    mha_out_proj,
     mha_fwd_splitkv,
     mha_fwd_splitkv_splits,
     mha_fwd,

@@ -27,7 +27,7 @@ MHA_DTYPE_BF16 = 1
 
 # Every symbol include/mha.h declares.
 EXPORTED_SYMBOLS = ("mha_fwd", "mha_fwd_splitkv", "mha_fwd_splitkv_splits", "mha_bwd",
-                    "mha_kl_fwd", "mha_status_string", "mha_abi_version")
+                    "mha_kl_fwd", "mha_out_proj", "mha_status_string", "mha_abi_version")
 
 _lib = None
 
@@ -68,6 +68,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+    ]
+    lib.mha_out_proj.restype = ctypes.c_int
+    lib.mha_out_proj.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
     ]
     lib.mha_bwd.restype = ctypes.c_int
     lib.mha_bwd.argtypes = [
@@ -178,6 +183,45 @@ def attention_kl(q1, k1, q2, k2, causal: bool = False, scale: float | None = Non
     if st != MHA_OK:
         raise MhaError(st, "mha_kl_fwd")
     return kl, lse1, lse2
+
+
+def mha_out_proj(o: int, w: int, bias: int | None, y: int, B: int, Nq: int, H: int, d: int, E: int,
+                 stream: int | None, dtype: int) -> int:
+    """Call the C entry point with raw pointers; returns the status code."""
+    return int(load_library().mha_out_proj(o, w, bias, y, B, Nq, H, d, E, stream, int(dtype)))
+
+
+def out_proj(o, w, bias=None, stream=None):
+    """Y [B, Nq, E] = concat_heads(O) W^T (+ bias) for device tensors.
+
+    o: [B, Nq, H, d] (e.g. from ``attention``); w: [E, H*d]; bias: [E] or
+    None; one dtype (float16 or bfloat16), contiguous, on one HIP device.
+    """
+    import torch
+
+    if o.dim() != 4 or w.dim() != 2:
+        raise ValueError("o must be [B, Nq, H, d] and w [E, H*d]")
+    B, Nq, H, d = o.shape
+    E = w.shape[0]
+    if w.shape[1] != H * d:
+        raise ValueError(f"w must be [E, {H * d}], got {tuple(w.shape)}")
+    tensors = [o, w] + ([bias] if bias is not None else [])
+    if any(t.dtype != o.dtype for t in tensors) or o.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("o, w and bias must share dtype float16 or bfloat16")
+    if any(not t.is_cuda or t.device != o.device or not t.is_contiguous() for t in tensors):
+        raise ValueError("o, w and bias must be contiguous tensors on one GPU device")
+    if bias is not None and bias.shape != (E,):
+        raise ValueError("bias must be [E]")
+    y = torch.empty((B, Nq, E), dtype=o.dtype, device=o.device)
+    dt = MHA_DTYPE_BF16 if o.dtype == torch.bfloat16 else MHA_DTYPE_FP16
+    with torch.cuda.device(o.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(o.device).cuda_stream
+        st = mha_out_proj(o.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                          y.data_ptr(), B, Nq, H, d, E, stream, dt)
+    if st != MHA_OK:
+        raise MhaError(st, "mha_out_proj")
+    return y
 
 
 def mha_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,

@@ -1,7 +1,7 @@
 /*
  * mha.h -- C ABI of the fused multi-head attention forward (whole, or split
- * over the keys for decoding), its backward and the fused attention KL
- * divergence, for AMD MI355X (gfx950 / CDNA4).
+ * over the keys for decoding), its backward, the fused attention KL
+ * divergence and the output projection, for AMD MI355X (gfx950 / CDNA4).
  *
  * The operation (per batch b and head h) is
  *
@@ -164,6 +164,35 @@ MHA_API mha_status_t mha_kl_fwd(const void* q1, const void* k1, const void* q2,
                                 const void* k2, float* kl, float* lse1, float* lse2, int B,
                                 int H, int Nq, int Nk, int d, int causal, float scale,
                                 void* stream, int dtype);
+
+/*
+ * mha_out_proj -- output projection after attention: Y = concat_heads(O) W^T
+ * (+ bias).
+ *
+ * "SparkAttention", MHA-Forward passage (Eq. 1): the heads' outputs are
+ * concatenated and multiplied by the output weight. O as written by mha_fwd,
+ * [B, Nq, H, d], is already that concatenation when read as
+ * [B*Nq, H*d], so no reshuffle is needed:
+ *
+ *     Y[t, e] = sum_{h, c} O[t, h, c] W[e, h*d + c]  (+ bias[e]),  t < B*Nq
+ *
+ * Arguments
+ *   o      device pointer, [B, Nq, H, d], element type `dtype`, 16-byte aligned
+ *   w      device pointer, [E, H*d] (one output feature per row),
+ *          `dtype`, 16-byte aligned
+ *   bias   device pointer, [E], `dtype`, 8-byte aligned; or NULL for none
+ *   y      device pointer, [B, Nq, E], `dtype` (written; fp32 accumulation
+ *          rounded to nearest even), 16-byte aligned
+ *   B, Nq, H, d, E  sizes, >= 0; H*d must be a multiple of 64 and E of 4
+ *                   (else MHA_ERR_UNSUPPORTED)
+ *   stream, dtype   as for mha_fwd
+ *
+ * Ownership, execution and errors: as for mha_fwd (one kernel enqueued; the
+ * library allocates nothing; y must not overlap o, w or bias). An empty
+ * problem (B*Nq == 0 or E == 0) returns MHA_OK and enqueues nothing.
+ */
+MHA_API mha_status_t mha_out_proj(const void* o, const void* w, const void* bias, void* y,
+                                  int B, int Nq, int H, int d, int E, void* stream, int dtype);
 
 /*
  * mha_bwd -- attention backward: writes dQ, dK, dV and D.

@@ -274,3 +274,43 @@ def test_kl_no_device_reports_device_error(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert call_kl() == mha.MHA_ERR_DEVICE
+
+
+# ------------------------------------------------------------- mha_out_proj
+PO, PW, PB, PY = (0x10000000 * (i + 40) for i in range(4))
+GOOD_PROJ = dict(o=PO, w=PW, bias=PB, y=PY, B=1, Nq=100, H=8, d=128, E=1024, stream=None,
+                 dtype=mha.MHA_DTYPE_BF16)
+
+
+def call_proj(**kw):
+    a = dict(GOOD_PROJ)
+    a.update(kw)
+    return mha.mha_out_proj(*(a[n] for n in ("o", "w", "bias", "y", "B", "Nq", "H", "d", "E",
+                                           "stream", "dtype")))
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(o=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(w=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(y=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(o=PO + 8), mha.MHA_ERR_INVALID_ARG),
+    (dict(y=PY + 8), mha.MHA_ERR_INVALID_ARG),
+    (dict(bias=PB + 4), mha.MHA_ERR_INVALID_ARG),
+    (dict(H=3, d=48), mha.MHA_ERR_UNSUPPORTED),     # H*d = 144, not a multiple of 64
+    (dict(E=1022), mha.MHA_ERR_UNSUPPORTED),        # E not a multiple of 4
+    (dict(H=0), mha.MHA_ERR_INVALID_ARG),           # nothing to project from
+    (dict(dtype=9), mha.MHA_ERR_INVALID_ARG),
+    (dict(B=-1), mha.MHA_ERR_INVALID_ARG),
+    (dict(y=PO + 1024), mha.MHA_ERR_INVALID_ARG),   # output overlaps O
+    (dict(bias=PY + 64), mha.MHA_ERR_INVALID_ARG),  # bias inside the output
+], ids=lambda x: str(x))
+def test_proj_validation_rejects(lib, kw, want):
+    assert call_proj(**kw) == want
+
+
+def test_proj_empty_and_no_bias(lib):
+    assert call_proj(Nq=0, o=0, y=0) == mha.MHA_OK
+    assert call_proj(E=0) == mha.MHA_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert call_proj(bias=None) == mha.MHA_ERR_DEVICE  # a null bias is valid

@@ -1,0 +1,159 @@
+"""Parity of the output projection (mha_out_proj, through the C ABI) with the
+fp64 oracle (oracle/proj.py), on the GPU.
+
+Bar: per element |Y_gpu - Y_ref| <= 1.25 (u |Y_ref| + a + K 2^-24 S_ij), with
+u the unit roundoff of the output type (2^-8 bf16, 2^-11 fp16), a its
+subnormal floor (2^-25 fp16, 0 bf16), K = H*d and S = |O| |W|^T + |bias|:
+the fp32 sum of K exact products of 16-bit values (plus the bias) is within
+K 2^-24 S of the exact sum, and rounding the result to the output type adds
+u |Y|. RMS of the error <= 2u RMS(Y_ref) (output rounding alone gives about
+0.6u). Shapes cover ragged token and feature tiles (M and E not multiples of
+256), no bias, fp16 and bf16, both workloads at full size (sampled rows for
+the larger), and an end-to-end check after mha_fwd.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+@pytest.fixture(scope="module")
+def mha(torch_mod):
+    import head_attention_mha_amd as m
+    m.load_library()
+    return m
+
+
+def to_dev(torch, bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
+
+
+def to_bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_proj(torch, mha, ob, wb, bb, dtype):
+    o, w = to_dev(torch, ob, dtype), to_dev(torch, wb, dtype)
+    b = to_dev(torch, bb, dtype) if bb is not None else None
+    B, Nq, H, d = o.shape
+    E = w.shape[0]
+    y = torch.full((B, Nq, E), float("nan"), dtype=o.dtype, device="cuda")
+    dt = mha.MHA_DTYPE_BF16 if dtype == "bf16" else mha.MHA_DTYPE_FP16
+    st = mha.mha_out_proj(o.data_ptr(), w.data_ptr(), b.data_ptr() if b is not None else None,
+                          y.data_ptr(), B, Nq, H, d, E, torch.cuda.current_stream().cuda_stream, dt)
+    assert st == mha.MHA_OK, mha.mha_status_string(st)
+    torch.cuda.synchronize()
+    return to_bits(y)
+
+
+def check(y_bits, ob, wb, bb, dtype, rows=None, label=""):
+    o, w = wl.bits_to_f64(ob, dtype), wl.bits_to_f64(wb, dtype)
+    b = wl.bits_to_f64(bb, dtype) if bb is not None else None
+    B, Nq, H, d = o.shape
+    K = H * d
+    y = wl.bits_to_f64(y_bits, dtype).reshape(B * Nq, -1)
+    assert np.all(np.isfinite(y)), f"{label}: unwritten/non-finite Y"
+    X = o.reshape(B * Nq, K)
+    if rows is not None:
+        X, y = X[rows], y[rows]
+    ref = oracle.out_proj(X[None, :, None, :].reshape(1, len(X), 1, K), w, b)[0]
+    S = np.abs(X) @ np.abs(w).T + (np.abs(b)[None, :] if b is not None else 0.0)
+    u, a = (2.0 ** -8, 0.0) if dtype == "bf16" else (2.0 ** -11, 2.0 ** -25)
+    bound = 1.25 * (u * np.abs(ref) + a + K * 2.0 ** -24 * S)
+    err = np.abs(y - ref)
+    st = dict(worst_ratio=float((err / bound).max()), rms_err=float(np.sqrt((err ** 2).mean())),
+              rms_ref=float(np.sqrt((ref ** 2).mean())), max_err=float(err.max()))
+    sys.__stderr__.write(f"[proj-parity] {label}: {st}\n")
+    assert st["worst_ratio"] <= 1.0, f"{label}: element bound {st}"
+    assert st["rms_err"] <= 2 * u * st["rms_ref"], f"{label}: RMS bar {st}"
+    return st
+
+
+def _inputs(B, Nq, H, d, E, dtype, seed, bias=True):
+    w = wl.ProjWorkload("case", B, Nq, H, d, E, dtype, seed)
+    ob, wb, bb = wl.make_proj_inputs(w)
+    return ob, wb, (bb if bias else None)
+
+
+SHAPES = [
+    # B, Nq, H, d, E, dtype, bias
+    (1, 1, 1, 64, 4, "fp16", True),
+    (1, 7, 2, 64, 12, "bf16", False),
+    (2, 77, 4, 64, 260, "bf16", True),     # ragged tokens and features
+    (1, 300, 8, 128, 1024, "fp16", True),
+    (3, 129, 16, 64, 512, "bf16", False),
+    (1, 513, 1, 128, 200, "fp16", True),
+    (2, 256, 8, 128, 2048, "bf16", True),  # whole tiles, 8 | number of tiles
+]
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=lambda c: "B{}q{}H{}d{}E{}{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], "b" if c[6] else ""))
+def test_proj_shapes(torch_mod, mha, case):
+    B, Nq, H, d, E, dtype, bias = case
+    ob, wb, bb = _inputs(B, Nq, H, d, E, dtype, 900 + Nq + E, bias)
+    y = run_proj(torch_mod, mha, ob, wb, bb, dtype)
+    check(y, ob, wb, bb, dtype, label=str(case))
+
+
+@pytest.mark.parametrize("name", list(wl.PROJ_WORKLOADS))
+def test_proj_workloads(torch_mod, mha, name):
+    w = wl.PROJ_WORKLOADS[name]
+    ob, wb, bb = wl.make_proj_inputs(w)
+    y = run_proj(torch_mod, mha, ob, wb, bb, w.dtype)
+    M = w.B * w.Nq
+    rows = None
+    if M * w.E * w.H * w.d > 2 ** 34:
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M),
+                                         rng.choice(M, 512, replace=False)]))
+    check(y, ob, wb, bb, w.dtype, rows, name)
+
+
+def test_proj_after_attention(torch_mod, mha):
+    """mha_fwd's O feeds the projection directly (no copy): compared with the
+    oracle applied to that same O."""
+    torch = torch_mod
+    B, H, N, d, E = 2, 8, 200, 64, 512
+    qb, kb, vb = wl.random_inputs(B, H, N, N, d, "bf16", seed=91)
+    q, k, v = (to_dev(torch, x, "bf16") for x in (qb, kb, vb))
+    o, _ = mha.attention(q, k, v, causal=True, scale=0.125)
+    _, wb, bb = _inputs(1, 1, H, d, E, "bf16", 92)
+    y = mha.out_proj(o, to_dev(torch, wb, "bf16"), to_dev(torch, bb, "bf16"))
+    torch.cuda.synchronize()
+    check(to_bits(y), to_bits(o), wb, bb, "bf16", label="after attention")
+
+
+def test_proj_deterministic_and_errors(torch_mod, mha):
+    torch = torch_mod
+    ob, wb, bb = _inputs(1, 300, 4, 64, 256, "fp16", 93)
+    a = run_proj(torch, mha, ob, wb, bb, "fp16")
+    b = run_proj(torch, mha, ob, wb, bb, "fp16")
+    assert np.array_equal(a, b)
+    o = torch.zeros((1, 4, 3, 48), dtype=torch.float16, device="cuda")
+    w = torch.zeros((8, 144), dtype=torch.float16, device="cuda")
+    with pytest.raises(mha.MhaError) as e:
+        mha.out_proj(o, w)
+    assert e.value.status == mha.MHA_ERR_UNSUPPORTED

@@ -56,6 +56,20 @@ K1 are N1 and N2 rounded to the type; Q2 and K2 are Q1 + N3/2 and K1 + N4/2
 computed in float32 from the rounded Q1, K1 and rounded to the type (a
 perturbed copy, as a student near its teacher).
 
+Output-projection workloads (the attention output of the long and decoder
+shapes projected back to the model width H*d, "SparkAttention" Eq. 1):
+
+============  ==  =====  ==  ===  ====  =====  ====
+name          B   Nq     H   d    E     dtype  seed
+============  ==  =====  ==  ===  ====  =====  ====
+proj_long     1   16384  8   128  1024  bf16   9
+proj_decoder  4   2048   32  128  4096  bf16   10
+============  ==  =====  ==  ===  ====  =====  ====
+
+Recipe: from ``default_rng(seed)`` draw O [B, Nq, H, d] standard normal, W
+[E, H*d] standard normal times 1/sqrt(H*d), bias [E] standard normal times
+0.1 (float32, in that order), each rounded to the type.
+
 The backward's output gradient dO of a workload is drawn the same way from
 ``default_rng(seed + 1000)`` with the shape of Q ([B, Nq, H, d]) and rounded to
 the workload's type.
@@ -82,6 +96,9 @@ __all__ = [
     "DECODE_WORKLOADS",
     "KL_WORKLOADS",
     "make_kl_inputs",
+    "ProjWorkload",
+    "PROJ_WORKLOADS",
+    "make_proj_inputs",
 ]
 
 
@@ -146,6 +163,32 @@ KL_WORKLOADS: dict[str, Workload] = {
     for w in [
         Workload("kl_long", 1, 8, 16384, 16384, 128, "bf16", True, 7),
         Workload("kl_mid", 2, 16, 4096, 4096, 64, "fp16", False, 8),
+    ]
+}
+
+
+@dataclass(frozen=True)
+class ProjWorkload:
+    name: str
+    B: int
+    Nq: int
+    H: int
+    d: int
+    E: int
+    dtype: str
+    seed: int
+
+    @property
+    def flops(self) -> float:
+        """2 * (B*Nq) * (H*d) * E multiply-adds counted as two FLOPs."""
+        return 2.0 * self.B * self.Nq * self.H * self.d * self.E
+
+
+PROJ_WORKLOADS: dict[str, ProjWorkload] = {
+    w.name: w
+    for w in [
+        ProjWorkload("proj_long", 1, 16384, 8, 128, 1024, "bf16", 9),
+        ProjWorkload("proj_decoder", 4, 2048, 32, 128, 4096, "bf16", 10),
     ]
 }
 
@@ -254,3 +297,14 @@ def make_kl_inputs(w: Workload | str, noise: float = 0.5):
     q2 = round_bits(bits_to_f32(q1, w.dtype) + np.float32(noise) * n3, w.dtype)
     k2 = round_bits(bits_to_f32(k1, w.dtype) + np.float32(noise) * n4, w.dtype)
     return q1, k1, q2, k2
+
+
+def make_proj_inputs(w: ProjWorkload | str):
+    """O [B, Nq, H, d], W [E, H*d], bias [E] of a projection workload (uint16 bits)."""
+    if isinstance(w, str):
+        w = PROJ_WORKLOADS[w]
+    rng = np.random.default_rng(w.seed)
+    o = rng.standard_normal((w.B, w.Nq, w.H, w.d), dtype=np.float32)
+    wt = rng.standard_normal((w.E, w.H * w.d), dtype=np.float32) * np.float32(1 / math.sqrt(w.H * w.d))
+    b = rng.standard_normal(w.E, dtype=np.float32) * np.float32(0.1)
+    return round_bits(o, w.dtype), round_bits(wt, w.dtype), round_bits(b, w.dtype)
