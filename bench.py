@@ -248,6 +248,20 @@ def cpu_baseline_bwd(w: wl.Workload, qb, kb, vb, gb, target_s: float) -> dict:
     }
 
 
+def calib_copy(torch, mib: int, device) -> None:
+    """Three plain device-to-device copies of ``mib`` MiB: a hardware counter
+    of bytes read or written, taken over the same run, is scaled by what it
+    reads for these copies of known size."""
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"calibration copy: {n * 2} bytes read, {n * 2} bytes written per launch",
+          file=sys.stderr, flush=True)
+
+
 def bench_proj(args, torch, mha, w) -> int:
     """The output-projection pass (its own workload type: O, W, bias)."""
     ob, wb, bb = wl.make_proj_inputs(w)
@@ -263,6 +277,8 @@ def bench_proj(args, torch, mha, w) -> int:
         if st != mha.MHA_OK:
             raise mha.MhaError(st, "mha_out_proj")
 
+    if args.calib_copy_mib:
+        calib_copy(torch, args.calib_copy_mib, o.device)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -438,14 +454,7 @@ def main() -> int:
         step = kl_step
 
     if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20) // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device=q.device)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"calibration copy: {n * 2} bytes read, {n * 2} bytes written per launch",
-              file=sys.stderr, flush=True)
+        calib_copy(torch, args.calib_copy_mib, q.device)
 
     for _ in range(args.warmup):
         step()
