@@ -122,17 +122,40 @@ __global__ __launch_bounds__(proj::kThreads) void mha_proj_kernel(ProjParams p) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[eb][tb][r] = 0.f;
 
+  // All MFMAs of a stage in k-step order; the six operands of k-step ks + 1
+  // are read while the eight MFMAs of k-step ks issue (pinned below), so
+  // LDS latency hides behind MFMA work after the first k-step.
   auto compute = [&](const uint8_t* lw, const uint8_t* lx) __attribute__((always_inline)) {
+    constexpr int NKS = 4;
+    u32x4 wa[2][EB], xb[2][TB];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 xb[TB];
+    for (int eb = 0; eb < EB; ++eb) wa[0][eb] = *reinterpret_cast<const u32x4*>(lw + woff[eb][0]);
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) xb[tb] = *reinterpret_cast<const u32x4*>(lx + xoff[tb][ks]);
+    for (int tb = 0; tb < TB; ++tb) xb[0][tb] = *reinterpret_cast<const u32x4*>(lx + xoff[tb][0]);
 #pragma unroll
-      for (int eb = 0; eb < EB; ++eb) {
-        const u32x4 wa = *reinterpret_cast<const u32x4*>(lw + woff[eb][ks]);
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < NKS) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[eb][tb] = O_::mfma(wa, xb[tb], acc[eb][tb]);
+        for (int eb = 0; eb < EB; ++eb) wa[c ^ 1][eb] = *reinterpret_cast<const u32x4*>(lw + woff[eb][ks + 1]);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) xb[c ^ 1][tb] = *reinterpret_cast<const u32x4*>(lx + xoff[tb][ks + 1]);
+      }
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[eb][tb] = O_::mfma(wa[c][eb], xb[c][tb], acc[eb][tb]);
+    }
+    // pins: the first k-step's reads, then per k-step its MFMAs with the
+    // next k-step's reads spread among them (one read after each MFMA but
+    // the last two)
+    __builtin_amdgcn_sched_group_barrier(0x100, EB + TB, 0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int m = 0; m < EB * TB; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks + 1 < NKS && m < EB + TB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
   };
