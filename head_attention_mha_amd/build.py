@@ -31,6 +31,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # Packed fp32 VALU ops stay off: plain scalar fp32 code only.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: with accumulators in AGPRs the compiler moved
+    # every score block to VGPRs before its softmax (v_accvgpr_read).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-result",
 ]

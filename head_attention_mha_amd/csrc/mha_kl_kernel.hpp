@@ -18,8 +18,9 @@
 // owns one query row (two lanes per row, one per half of the keys, merged
 // with a cross-half exchange). Causal tiles past the frontier are skipped
 // (the page's causal handling); only diagonal and tail tiles carry an element
-// mask. The softmax state lives in the exp2 domain (scores times
-// scale * log2(e)).
+// mask. The maxima are kept on the raw scores and the sums in the exp2
+// domain (scores times scale * log2(e)), the scale entering each exponent
+// through one fused multiply-add.
 #pragma once
 
 #include "mha_fwd_kernel.hpp"
@@ -149,7 +150,9 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
     for (int i = 0; i < DK; ++i) roff[i] = key * ROWB + 16 * ((2 * i + hf) ^ sw);
   }
 
-  // running state of this lane's half of the row (m shared by both halves)
+  // running state of this lane's half of the row (m shared by both halves):
+  // maxima of the raw scores, sums in the exp2 domain relative to m * c,
+  // acc = sum exp2((S1 - m1) c) (S1 - S2) over raw score differences
   float m1 = NEG_INF, m2 = NEG_INF, l1 = 0.f, l2 = 0.f, acc = 0.f;
   const float c = p.scale_log2;
 
@@ -173,23 +176,29 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
       }
       sync::PinReads<0, 2 * DK, 1, 4>::apply();
       __builtin_amdgcn_sched_barrier(0);
-      // scores in the exp2 domain; element r is key
-      // j*BK + 32*kb + 16*(r>>3) + 8*hf + (r&7)
+      // raw scores; element r is key j*BK + 32*kb + 16*(r>>3) + 8*hf + (r&7).
+      // The maxima are taken on the raw scores (the scale is positive) and
+      // the scale enters once, inside each exponent's fused multiply-add.
       float x1[16], x2[16];
-      float t1 = NEG_INF, t2 = NEG_INF;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float a = s1[r] * c, e = s2[r] * c;
-        if constexpr (MASK) {
+        x1[r] = s1[r];
+        x2[r] = s2[r];
+      }
+      if constexpr (MASK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int key = j * BK + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
           const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
-          a = vis ? a : NEG_INF;
-          e = vis ? e : NEG_INF;
+          x1[r] = vis ? x1[r] : NEG_INF;
+          x2[r] = vis ? x2[r] : NEG_INF;
         }
-        x1[r] = a;
-        x2[r] = e;
-        t1 = fmaxf(t1, a);
-        t2 = fmaxf(t2, e);
+      }
+      float t1 = x1[0], t2 = x2[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        t1 = fmaxf(t1, x1[r]);
+        t2 = fmaxf(t2, x2[r]);
       }
       // a row may see no key of this block (causal, diagonal tile): then
       // its maximum stays as it was; the reference value 0 keeps the
@@ -198,18 +207,19 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
       const float n2 = fmaxf(m2, max_halves(t2));
       const float r1 = n1 == NEG_INF ? 0.f : n1;
       const float r2 = n2 == NEG_INF ? 0.f : n2;
-      const float al1 = fast_exp2(m1 - r1), al2 = fast_exp2(m2 - r2);
+      const float al1 = fast_exp2((m1 - r1) * c), al2 = fast_exp2((m2 - r2) * c);
       m1 = n1;
       m2 = n2;
+      const float r1c = r1 * c, r2c = r2 * c;
       float sl1 = 0.f, sl2 = 0.f, sa = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p1 = fast_exp2(x1[r] - r1);
-        const float p2 = fast_exp2(x2[r] - r2);
-        // the difference of the raw scores, then scaled: finite also for
-        // masked keys (where p1 = 0), and exactly 0 where the two scores
-        // are equal (no fused multiply-add can mix their roundings)
-        const float dx = (s1[r] - s2[r]) * c;
+        const float p1 = fast_exp2(__builtin_fmaf(x1[r], c, -r1c));
+        const float p2 = fast_exp2(__builtin_fmaf(x2[r], c, -r2c));
+        // the difference of the raw (unmasked, finite) scores; the scale is
+        // applied to acc once at the end. Exactly 0 where the two scores are
+        // equal.
+        const float dx = s1[r] - s2[r];
         sl1 += p1;
         sl2 += p2;
         sa = __builtin_fmaf(p1, dx, sa);
@@ -257,16 +267,16 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
   l2 = sum_halves(l2);
   acc = sum_halves(acc);
   if (hf == 0 && my_q < p.Nq) {
-    const float lse1 = (m1 + fast_log2(l1)) * kl::kLn2;
-    const float lse2 = (m2 + fast_log2(l2)) * kl::kLn2;
+    const float lse1 = __builtin_fmaf(m1, c, fast_log2(l1)) * kl::kLn2;
+    const float lse2 = __builtin_fmaf(m2, c, fast_log2(l2)) * kl::kLn2;
     const size_t r = (size_t)bh * p.Nq + my_q;
     p.lse1[r] = lse1;
     p.lse2[r] = lse2;
     // LSE2 - LSE1 from the differences of the maxima and of the log sums,
     // not of the two LSEs (no cancellation of two large values, and exactly
     // 0 for identical distributions)
-    const float dlse = (m2 - m1) + (fast_log2(l2) - fast_log2(l1));
-    p.kl[r] = (acc / l1 + dlse) * kl::kLn2;
+    const float dlse = (m2 - m1) * c + (fast_log2(l2) - fast_log2(l1));
+    p.kl[r] = (acc * c / l1 + dlse) * kl::kLn2;
   }
 }
 
