@@ -231,39 +231,71 @@ __global__ __launch_bounds__(split::kThreads) void mha_split_partial_kernel(Spli
 }
 
 // ---- merge of the splits ---------------------------------------------------------
-// One workgroup per row r = (b*H + h)*Nq + n: thread (g, c) handles channels
-// 4c .. 4c+3 of the splits s = g, g + G, ...; the G partial sums are added
-// through LDS.
+// One workgroup per row r = (b*H + h)*Nq + n. The merge is a few dependent
+// memory round trips on little data, so it is laid out for latency: thread
+// (g, c) first issues the loads of channels 4c .. 4c+3 of its splits
+// s = g + G*i (i < kPre), which do not depend on the weights; meanwhile
+// thread t < n_splits reads LSE_t, the workgroup takes their maximum M and
+// stores the weights w_s = exp(LSE_s - M) in LDS; then every thread adds
+// w_s * O_s over its splits and the G partial sums are added through LDS.
+// Empty splits have LSE = -inf and O = 0, weight 0.
 template <typename T, int D>
 __global__ __launch_bounds__(split::kThreads) void mha_split_merge_kernel(SplitParams p) {
   constexpr int TPR = D / 4;                   // channel threads per split group
   constexpr int G = split::kThreads / TPR;     // split groups
-  __shared__ float sm_max[G];
+  constexpr int NW = split::kThreads / 64;
+  constexpr int kPre = 8;                      // splits per group loaded up front
+  constexpr float NEG_INF = -__builtin_inff();
+  __shared__ float sm_w[split::kThreads];      // n_splits <= kThreads
+  __shared__ float sm_max[NW];
   __shared__ float sm_l[G];
   __shared__ float sm_o[G][D];
   const long long r = blockIdx.x;
   const long long n_rows = (long long)p.B * p.H * p.Nq;
+  const int n = p.n_splits;
   const int tid = threadIdx.x;
   const int g = tid / TPR;
   const int c4 = (tid - g * TPR) * 4;
-  float M = -__builtin_inff();
-  for (int s = g; s < p.n_splits; s += G) M = fmaxf(M, p.lse_part[s * n_rows + r]);
-  if (c4 == 0) sm_max[g] = M;
-  __syncthreads();
+  float4 x[kPre];
 #pragma unroll
-  for (int t = 0; t < G; ++t) M = fmaxf(M, sm_max[t]);
+  for (int i = 0; i < kPre; ++i) {
+    const int s = g + G * i;
+    x[i] = s < n ? *reinterpret_cast<const float4*>(p.o_part + (s * n_rows + r) * D + c4)
+                 : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float ls = tid < n ? p.lse_part[tid * n_rows + r] : NEG_INF;
+  float M = ls;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((tid & 63) == 0) sm_max[tid >> 6] = M;
+  __syncthreads();
+  M = sm_max[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_max[w]);
+  if (tid < n) sm_w[tid] = ls == NEG_INF ? 0.f : __expf(ls - M);
+  __syncthreads();
   float L = 0.f;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = g; s < p.n_splits; s += G) {
-    const float ls = p.lse_part[s * n_rows + r];
-    if (ls == -__builtin_inff()) continue;
-    const float w = __expf(ls - M);
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int s = g + G * i;
+    if (s < n) {
+      const float w = sm_w[s];
+      L += w;
+      o[0] = __builtin_fmaf(w, x[i].x, o[0]);
+      o[1] = __builtin_fmaf(w, x[i].y, o[1]);
+      o[2] = __builtin_fmaf(w, x[i].z, o[2]);
+      o[3] = __builtin_fmaf(w, x[i].w, o[3]);
+    }
+  }
+  for (int s = g + G * kPre; s < n; s += G) {
+    const float w = sm_w[s];
     L += w;
-    const float4 x = *reinterpret_cast<const float4*>(p.o_part + (s * n_rows + r) * D + c4);
-    o[0] = __builtin_fmaf(w, x.x, o[0]);
-    o[1] = __builtin_fmaf(w, x.y, o[1]);
-    o[2] = __builtin_fmaf(w, x.z, o[2]);
-    o[3] = __builtin_fmaf(w, x.w, o[3]);
+    const float4 y = *reinterpret_cast<const float4*>(p.o_part + (s * n_rows + r) * D + c4);
+    o[0] = __builtin_fmaf(w, y.x, o[0]);
+    o[1] = __builtin_fmaf(w, y.y, o[1]);
+    o[2] = __builtin_fmaf(w, y.z, o[2]);
+    o[3] = __builtin_fmaf(w, y.w, o[3]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) sm_o[g][c4 + i] = o[i];
@@ -275,17 +307,17 @@ __global__ __launch_bounds__(split::kThreads) void mha_split_merge_kernel(SplitP
   for (int t = 0; t < G; ++t) L += sm_l[t];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float x = 0.f;
+    float v = 0.f;
 #pragma unroll
-    for (int t = 0; t < G; ++t) x += sm_o[t][c4 + i];
-    o[i] = x;
+    for (int t = 0; t < G; ++t) v += sm_o[t][c4 + i];
+    o[i] = v;
   }
   const float inv = 1.f / L;
   // O is laid out [b][n][h]: r = bh*Nq + n
   const long long bh = r / p.Nq;
-  const int n = (int)(r - bh * p.Nq);
+  const int nq = (int)(r - bh * p.Nq);
   const int b = (int)(bh / p.H), h = (int)(bh - (long long)b * p.H);
-  uint16_t* dst = p.o + (((size_t)b * p.Nq + n) * p.H + h) * D + c4;
+  uint16_t* dst = p.o + (((size_t)b * p.Nq + nq) * p.H + h) * D + c4;
   u32x2 w2;
   w2[0] = Ops<T>::pack(o[0] * inv, o[1] * inv);
   w2[1] = Ops<T>::pack(o[2] * inv, o[3] * inv);

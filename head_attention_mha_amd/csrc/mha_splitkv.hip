@@ -8,6 +8,7 @@ using namespace mha_host;
 namespace {
 
 constexpr int kMaxSplits = 256;
+static_assert(kMaxSplits <= mha::split::kThreads, "the merge reads one LSE per thread");
 // Keys per split are a multiple of this (the partial kernel's block at d = 64).
 constexpr int kSplitAlign = 256;
 
