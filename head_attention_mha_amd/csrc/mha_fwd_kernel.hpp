@@ -229,15 +229,22 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   constexpr int NCPW = TILEB / 1024 / kWaves;  // 1 KiB copies per wave per tensor
   static_assert(NCPW >= 1, "tile too small for the workgroup");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[TILEB];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[TILEB];
   // V^T tiles: row d holds the tile's 64 keys of head-dim index d (128
   // bytes) plus 16 bytes of padding, which keeps both the transposed writes
   // and the MFMA operand reads free of bank conflicts
   constexpr int VT_RS = 2 * BK + 16;
   constexpr int VTB = D * VT_RS;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_vt0[VTB];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_vt1[VTB];
+  constexpr int VTB_AL = (VTB + 1023) / 1024 * 1024;
+  constexpr int OSB = 32 * ROWB;  // one wave's 32 output rows
+  // One LDS allocation laid out by hand: the K and V^T tiles first, so the
+  // GEMM phases address them with immediate offsets (below 64 KiB), then one
+  // output-staging slot per wave for the epilogue.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * TILEB + 2 * VTB_AL + kWaves * OSB];
+  uint8_t* const lds_k0 = lds;
+  uint8_t* const lds_k1 = lds + TILEB;
+  uint8_t* const lds_vt0 = lds + 2 * TILEB;
+  uint8_t* const lds_vt1 = lds + 2 * TILEB + VTB_AL;
+  uint8_t* const lds_o = lds + 2 * TILEB + 2 * VTB_AL;
 
   // ---- work item: (batch, head, query tile) --------------------------------
   // Workgroups are dispatched in index order, round-robin over the 8 XCDs.
@@ -252,8 +259,15 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   const bool by_xcd = (BH & 7) == 0;
   const int k = by_xcd ? lin >> 3 : lin;
   const int nh = by_xcd ? BH >> 3 : BH;
-  const int qi = k / nh;
-  const int hh = k - qi * nh;
+  // Heads are taken in groups of G, enough for the query tiles of one group
+  // to fill the XCD's 32 CUs (or all 256): the workgroups running at one
+  // time then stream the K/V of only G heads, which stay in L2.
+  const int G = min(nh, max(1, ((by_xcd ? 32 : 256) + p.n_qtiles - 1) / p.n_qtiles));
+  const int g = k / (G * p.n_qtiles);
+  const int gr = k - g * (G * p.n_qtiles);
+  const int gn = min(G, nh - g * G);  // heads in this group (the last may be short)
+  const int qi = gr / gn;
+  const int hh = g * G + (gr - qi * gn);
   const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;
   const int qt = CAUSAL ? p.n_qtiles - 1 - qi : qi;
   const int b = bh / p.H;
@@ -572,13 +586,12 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   if (grp == 0) {
     // group A: phase 2j = GEMM(j), phase 2j+1 = softmax(j)
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
-      issue_k_next(j, buf);     // start of phase 2j
+      issue_k_next(j, buf);     // start of period j
       gemm_phase(j, buf);
-      barrier();                // #2j+1
-      write_v(j, buf);          // start of phase 2j+1
+      write_v(j, buf);
       softmax(j);
       wait_k(j + 1 < n_kt);
-      barrier();                // #2j+2
+      barrier();                // end of period j
     };
     int j = 0;
     for (; j + 1 < n_kt; j += 2) {
@@ -589,25 +602,22 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       tile(j, I0{});
       ++j;
     }
-    // phase 2n: P.V of the last tile, then barrier #2n+1 to match group B
+    // P.V of the last tile
     if (j & 1) gemm_phase(j, I1{});
     else gemm_phase(j, I0{});
-    barrier();
   } else {
     // group B: phase 2j+1 = GEMM(j), phase 2j+2 = softmax(j)
-    issue_k_next(0, I0{});      // start of phase 0
-    barrier();                  // #1
+    issue_k_next(0, I0{});      // start of period 0
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
-      write_v(j, buf);          // start of phase 2j+1
+      write_v(j, buf);
       gemm_phase(j, buf);
       wait_k(j + 1 < n_kt);
-      barrier();                // #2j+2
+      barrier();                // end of period j
       if constexpr (decltype(buf)::value == 0)
-        issue_k_next(j + 1, I1{});  // start of phase 2j+2
+        issue_k_next(j + 1, I1{});  // start of period j+1
       else
         issue_k_next(j + 1, I0{});
       softmax(j);
-      barrier();                // #2j+3
     };
     int j = 0;
     for (; j + 1 < n_kt; j += 2) {
@@ -624,10 +634,18 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale*m + ln(l) ------------------------
+  // Each lane holds one query row's O as 8-byte pieces spread over the row;
+  // written out directly they would be 16 scattered partial-line writes per
+  // lane. They go through the wave's LDS slot instead (row ln, 16-byte
+  // chunk c at c ^ (ln mod CH) so the writes spread over the banks) and
+  // leave as 16-byte stores that cover whole rows. The buffer's range check
+  // drops rows past Nq.
   const float l_tot = sum_halves(l_run);
-  if (my_q < p.Nq) {
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = Ob + (size_t)my_q * rs;
+  const float inv = 1.f / l_tot;
+  uint8_t* const slot = lds_o + wave * OSB;
+  {
+    const uint32_t y = (uint32_t)(ln & (CH - 1));
+    const uint32_t wa = (uint32_t)(ln * ROWB + 8 * hf);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -635,12 +653,27 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
         u32x2 w2;
         w2[0] = O_::pack(o[db][4 * a + 0] * inv, o[db][4 * a + 1] * inv);
         w2[1] = O_::pack(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * hf) = w2;
+        *reinterpret_cast<u32x2*>(slot + wa + 16 * (y ^ (uint32_t)(4 * db + a))) = w2;
       }
-    if (hf == 0) {
-      const float lse = m_run * p.scale + fast_log2(l_tot) * 0.69314718055994531f;
-      p.lse[((size_t)b * p.H + h) * p.Nq + my_q] = lse;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  {
+    // copy c reads slot rows c*RPC + lane/CH, physical chunk lane % CH
+    constexpr int RPC = 1024 / ROWB;
+    const int nrows = min(kBQ, p.Nq - q0);
+    const auto o_rs = make_rsrc(Ob + (size_t)q0 * rs, (uint32_t)(nrows - 1) * row_bytes + ROWB);
+    const uint32_t rl = lane / CH, pc = lane % CH;
+    const uint32_t gbase = (uint32_t)(wave * 32 + rl) * row_bytes;
+#pragma unroll
+    for (int c = 0; c < OSB / 1024; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(slot + c * 1024 + 16 * lane);
+      const uint32_t lc = (pc ^ ((uint32_t)(c * RPC) + rl)) & (CH - 1);  // logical chunk
+      __builtin_amdgcn_raw_buffer_store_b128(w, o_rs, gbase + (uint32_t)(c * RPC) * row_bytes + 16 * lc, 0, 0);
     }
+  }
+  if (my_q < p.Nq && hf == 0) {
+    const float lse = m_run * p.scale + fast_log2(l_tot) * 0.69314718055994531f;
+    p.lse[((size_t)b * p.H + h) * p.Nq + my_q] = lse;
   }
 }
 
