@@ -29,8 +29,10 @@
 // * Ping-pong of two wave groups. Waves 0-3 and 4-7 each alternate a GEMM
 //   phase (P.V of the previous tile and S^T of the current tile, 32 MFMAs)
 //   and a softmax phase (VALU), the second group half a period behind the
-//   first, with workgroup barriers between phases: every SIMD holds one wave
-//   of each group, so one issues MFMAs while the other runs its softmax.
+//   first: every SIMD holds one wave of each group, so one issues MFMAs
+//   while the other runs its softmax. One workgroup barrier per key tile
+//   (period) covers the reuse of the K and V^T buffers; within a period the
+//   groups are not forced into step.
 // * S is computed transposed (keys are MFMA rows, queries are columns), so
 //   each lane owns one query: the row max needs one exchange between lanes
 //   l and l^32, the row sum needs none until the end, and alpha is a
@@ -57,8 +59,11 @@
 //   in exact arithmetic, and the rescale then runs only when the max jumps.
 // * The 1-D grid is remapped so that all query tiles of a head run on one
 //   XCD (workgroups are dispatched round-robin over the 8 XCDs), keeping the
-//   head's K/V in that XCD's L2, and so that each XCD starts its heaviest
-//   causal query tiles (of all its heads) first.
+//   head's K/V in that XCD's L2; heads are taken in groups small enough for
+//   their K/V to stay in L2 while in flight; each XCD starts its heaviest
+//   causal query tiles first, ordered for its four shader engines.
+// * The epilogue stages each wave's O rows in LDS and writes whole rows
+//   with 16-byte stores.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -519,27 +524,26 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     l_run += rsum[0];
   };
 
-  // ---- phase schedule ------------------------------------------------------
-  // The workgroup steps through phases separated by barriers #0, #1, ...;
-  // phase p runs between barriers #p and #p+1. Group A (grp 0) runs the
-  // GEMM phase of tile j in phase 2j and its softmax phase in phase 2j+1;
-  // group B runs the same sequence one phase later, so on every SIMD one
-  // wave issues MFMAs while the other runs its softmax. Each group has its
-  // own straight-line loop; the k-th barrier of every wave pairs up.
-  // K_j is read in phases 2j and 2j+1, V_j in phases 2j+2 and 2j+3.
-  // * At the start of each even phase 2m every wave starts its share of the
-  //   LDS copy of K_{m+1}, into the K buffer that held K_{m-1} (last read in
-  //   phase 2m-1); it is waited for before barrier #2m+2.
-  // * At the start of each odd phase 2m+1 every copying wave writes V_m
-  //   (already in registers) transposed into the V^T buffer that held V_{m-2}
-  //   (last read in phase 2m-1), then starts loading V_{m+1} into the same
-  //   registers, two phases ahead of its write.
-  // Vector-memory loads retire in order, so before barrier #2m+2 a wait that
+  // ---- period schedule -----------------------------------------------------
+  // Key tile j takes period j, between barrier #j (#0 ends the prologue)
+  // and barrier #j+1. Group A (grp 0) runs the GEMM phase of tile j and then
+  // its softmax in period j; group B runs the softmax of tile j-1 and then
+  // the GEMM phase of tile j, so on every SIMD one wave issues MFMAs while
+  // the other runs its softmax. Each group has its own straight-line loop;
+  // the k-th barrier of every wave pairs up. K_j is read in period j, V_j
+  // in period j+1.
+  // * At the start of period m every wave starts its share of the LDS copy
+  //   of K_{m+1}, into the K buffer that held K_{m-1} (last read in period
+  //   m-1); it is waited for before barrier #m+1.
+  // * In period m every copying wave writes V_m (already in registers)
+  //   transposed into the V^T buffer that held V_{m-2} (last read in period
+  //   m-1), then starts loading V_{m+1} into the same registers.
+  // Vector-memory loads retire in order, so before barrier #m+1 a wait that
   // leaves only the two newest loads (V_{m+1}) outstanding covers K_{m+1}.
   // Workgroup barrier without a memory fence: __syncthreads() also releases
   // memory at workgroup scope, which would make each wave wait at every
-  // barrier for the K copy it started at the beginning of the phase. The
-  // waits that matter are explicit (wait_k: the copies the next phase reads
+  // barrier for the K copy it started at the beginning of the period. The
+  // waits that matter are explicit (wait_k: the copies the next period reads
   // and this wave's LDS writes); the empty asm statements keep the compiler
   // from moving LDS accesses across the barrier.
   auto barrier = [&]() __attribute__((always_inline)) {
@@ -561,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     }
   };
   // Write V_m into V^T buffer m & 1 = BUF, then start loading V_{m+1}. The
-  // V_m loads are older than the K_{m+1} copy issued at the start of phase 2m.
+  // V_m loads are older than the K_{m+1} copy issued at the start of period m.
   auto write_v = [&](int m, auto buf) __attribute__((always_inline)) {
     if (m >= n_kt) return;
     if (m + 1 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70 | NCPW);  // vmcnt(NCPW)
@@ -591,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   wait_k(true);  // K_0 landed; V_0 may be in flight
   barrier();     // #0
   if (grp == 0) {
-    // group A: phase 2j = GEMM(j), phase 2j+1 = softmax(j)
+    // group A: period j = GEMM(j), write V_j, softmax(j)
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
       issue_k_next(j, buf);     // start of period j
       gemm_phase(j, buf);
@@ -613,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     if (j & 1) gemm_phase(j, I1{});
     else gemm_phase(j, I0{});
   } else {
-    // group B: phase 2j+1 = GEMM(j), phase 2j+2 = softmax(j)
+    // group B: period j = softmax(j-1), write V_j, GEMM(j)
     issue_k_next(0, I0{});      // start of period 0
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
       write_v(j, buf);
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       tile(j, I0{});
       ++j;
     }
-    // phase 2n+1: P.V of the last tile
+    // P.V of the last tile
     if (j & 1) gemm_phase(j, I1{});
     else gemm_phase(j, I0{});
   }
