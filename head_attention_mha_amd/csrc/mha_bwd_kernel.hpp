@@ -193,8 +193,9 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
   const int lin = blockIdx.x;
   const int BH = p.B * p.H;
   const bool by_xcd = (BH & 7) == 0;
-  const int kk = by_xcd ? lin >> 3 : lin;
   const int nh = by_xcd ? BH >> 3 : BH;
+  // two (d = 128) or three (d = 64) workgroups per CU
+  const int kk = by_xcd ? engine_order(lin >> 3, nh * p.n_tiles, D == 128 ? 64 : 96) : lin;
   const int qi = kk / nh;
   const int hh = kk - qi * nh;
   const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;
@@ -422,8 +423,9 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   const int lin = blockIdx.x;
   const int BH = p.B * p.H;
   const bool by_xcd = (BH & 7) == 0;
-  const int kk = by_xcd ? lin >> 3 : lin;
   const int nh = by_xcd ? BH >> 3 : BH;
+  // one (d = 128) or two (d = 64) workgroups per CU
+  const int kk = by_xcd ? engine_order(lin >> 3, nh * p.n_tiles, D == 128 ? 32 : 64) : lin;
   const int ki = kk / nh;
   const int hh = kk - ki * nh;
   const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;

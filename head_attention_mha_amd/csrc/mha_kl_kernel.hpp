@@ -77,8 +77,9 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
   const int lin = blockIdx.x;
   const int BH = p.B * p.H;
   const bool by_xcd = (BH & 7) == 0;
-  const int kk = by_xcd ? lin >> 3 : lin;
   const int nh = by_xcd ? BH >> 3 : BH;
+  // two workgroups per CU
+  const int kk = by_xcd ? engine_order(lin >> 3, nh * p.n_tiles, 64) : lin;
   const int qi = kk / nh;
   const int hh = kk - qi * nh;
   const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;
