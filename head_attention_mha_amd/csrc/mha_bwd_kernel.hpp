@@ -376,18 +376,16 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
   run(jm, j_end, std::integral_constant<int, 1>{});
   run(j_end, n_kt, std::integral_constant<int, 0>{});
 
-  // dQ = scale * dQ^T, rounded to the I/O type
-  if (my_q < p.Nq) {
-    uint16_t* row = p.dq + qo + (size_t)my_q * rs;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 w2;
-        w2[0] = O_::pack(dq[db][4 * a + 0] * p.scale, dq[db][4 * a + 1] * p.scale);
-        w2[1] = O_::pack(dq[db][4 * a + 2] * p.scale, dq[db][4 * a + 3] * p.scale);
-        *reinterpret_cast<u32x2*>(row + db * 32 + 8 * a + 4 * hf) = w2;
-      }
+  // dQ = scale * dQ^T, rounded to the I/O type, stored as whole rows through
+  // the K tile buffers (free once every wave has left the tile loop; no copy
+  // is in flight)
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+  sync::bare_barrier();
+  {
+    const int nrows = min(kBQ, p.Nq - q0);
+    const auto out = make_rsrc(p.dq + qo + (size_t)q0 * rs, (uint32_t)(nrows - 1) * row_bytes + 2 * D);
+    uint8_t* const slot = (wave < 2 ? lds_k0 : lds_k1) + (wave & 1) * 32 * 2 * D;
+    store_rows<O_, D>(dq, p.scale, slot, out, (uint32_t)(wave * 32) * row_bytes, row_bytes, lane);
   }
 }
 
@@ -621,22 +619,20 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   }
   run(f + (CAUSAL ? 1 : 0), n_t, std::integral_constant<int, 2>{});
 
-  // dK = scale * dK^T, dV = dV^T (lane = key, registers = head-dim index)
-  if (my_k < p.Nk) {
-    uint16_t* krow = p.dk + kvo + (size_t)my_k * rs;
-    uint16_t* vrow = p.dv + kvo + (size_t)my_k * rs;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 wk, wv;
-        wk[0] = O_::pack(dkt[db][4 * a + 0] * p.scale, dkt[db][4 * a + 1] * p.scale);
-        wk[1] = O_::pack(dkt[db][4 * a + 2] * p.scale, dkt[db][4 * a + 3] * p.scale);
-        wv[0] = O_::pack(dvt[db][4 * a + 0], dvt[db][4 * a + 1]);
-        wv[1] = O_::pack(dvt[db][4 * a + 2], dvt[db][4 * a + 3]);
-        *reinterpret_cast<u32x2*>(krow + db * 32 + 8 * a + 4 * hf) = wk;
-        *reinterpret_cast<u32x2*>(vrow + db * 32 + 8 * a + 4 * hf) = wv;
-      }
+  // dK = scale * dK^T, dV = dV^T (lane = key, registers = head-dim index),
+  // stored as whole rows through one Q/dO tile buffer per wave (free once
+  // every wave has left the tile loop; no copy is in flight)
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+  sync::bare_barrier();
+  {
+    const int nrows = min(kBKV, p.Nk - k0);
+    const uint32_t range = (uint32_t)(nrows - 1) * row_bytes + 2 * D;
+    const auto out_k = make_rsrc(p.dk + kvo + (size_t)k0 * rs, range);
+    const auto out_v = make_rsrc(p.dv + kvo + (size_t)k0 * rs, range);
+    uint8_t* const slot = wave == 0 ? lds_q0 : wave == 1 ? lds_q1 : wave == 2 ? lds_g0 : lds_g1;
+    const uint32_t gbase = (uint32_t)(wave * 32) * row_bytes;
+    store_rows<O_, D>(dkt, p.scale, slot, out_k, gbase, row_bytes, lane);
+    store_rows<O_, D>(dvt, 1.f, slot, out_v, gbase, row_bytes, lane);
   }
 }
 

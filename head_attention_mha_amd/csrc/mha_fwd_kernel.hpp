@@ -209,6 +209,41 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
                                            16, voffset, 0, 0, 0);
 }
 
+// One wave's 32 output rows, held in MFMA-accumulator layout (lane (ln, hf)
+// owns row ln; value r of block db is column 32db + 8(r/4) + 4hf + r%4),
+// scaled by `mul`, rounded to the I/O type and written out through an LDS
+// slot of 32 * 2D bytes: each lane's eight-byte pieces, scattered over its
+// row, are staged (row ln, 16-byte chunk c at chunk c ^ (ln mod D/8), which
+// spreads the writes over the banks) and leave as 16-byte buffer stores
+// that cover whole rows. `gbase` is the byte offset of the wave's first row
+// in the buffer `out`; rows past its range are dropped by the range check.
+template <typename Ops_, int D>
+__device__ __forceinline__ void store_rows(const f32x16* acc, float mul, uint8_t* slot,
+                                           __amdgpu_buffer_rsrc_t out, uint32_t gbase,
+                                           uint32_t row_bytes, int lane) {
+  constexpr int DB = D / 32, CH = D / 8, ROWB = 2 * D, RPC = 1024 / ROWB, NC = 32 * ROWB / 1024;
+  const int ln = lane & 31, hf = lane >> 5;
+  const uint32_t y = (uint32_t)(ln & (CH - 1)), wa = (uint32_t)(ln * ROWB + 8 * hf);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      u32x2 w2;
+      w2[0] = Ops_::pack(acc[db][4 * a + 0] * mul, acc[db][4 * a + 1] * mul);
+      w2[1] = Ops_::pack(acc[db][4 * a + 2] * mul, acc[db][4 * a + 3] * mul);
+      *reinterpret_cast<u32x2*>(slot + wa + 16 * (y ^ (uint32_t)(4 * db + a))) = w2;
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot is written
+  // copy c reads slot rows c*RPC + lane/CH at physical chunk lane % CH
+  const uint32_t rl = (uint32_t)lane / CH, pc = (uint32_t)lane % CH;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(slot + c * 1024 + 16 * lane);
+    const uint32_t lc = (pc ^ ((uint32_t)(c * RPC) + rl)) & (CH - 1);  // logical chunk
+    __builtin_amdgcn_raw_buffer_store_b128(w, out, gbase + ((uint32_t)(c * RPC) + rl) * row_bytes + 16 * lc, 0, 0);
+  }
+}
+
 // Scheduling pins for the GEMM phase: the reads of the first AHEAD operands,
 // then for every MFMA n one MFMA followed by the 16-byte read of operand
 // n+AHEAD.
@@ -659,34 +694,10 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // drops rows past Nq.
   const float l_tot = sum_halves(l_run);
   const float inv = 1.f / l_tot;
-  uint8_t* const slot = lds_o + wave * OSB;
   {
-    const uint32_t y = (uint32_t)(ln & (CH - 1));
-    const uint32_t wa = (uint32_t)(ln * ROWB + 8 * hf);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 w2;
-        w2[0] = O_::pack(o[db][4 * a + 0] * inv, o[db][4 * a + 1] * inv);
-        w2[1] = O_::pack(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
-        *reinterpret_cast<u32x2*>(slot + wa + 16 * (y ^ (uint32_t)(4 * db + a))) = w2;
-      }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  {
-    // copy c reads slot rows c*RPC + lane/CH, physical chunk lane % CH
-    constexpr int RPC = 1024 / ROWB;
     const int nrows = min(kBQ, p.Nq - q0);
     const auto o_rs = make_rsrc(Ob + (size_t)q0 * rs, (uint32_t)(nrows - 1) * row_bytes + ROWB);
-    const uint32_t rl = lane / CH, pc = lane % CH;
-    const uint32_t gbase = (uint32_t)(wave * 32 + rl) * row_bytes;
-#pragma unroll
-    for (int c = 0; c < OSB / 1024; ++c) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(slot + c * 1024 + 16 * lane);
-      const uint32_t lc = (pc ^ ((uint32_t)(c * RPC) + rl)) & (CH - 1);  // logical chunk
-      __builtin_amdgcn_raw_buffer_store_b128(w, o_rs, gbase + (uint32_t)(c * RPC) * row_bytes + 16 * lc, 0, 0);
-    }
+    store_rows<O_, D>(o, inv, lds_o + wave * OSB, o_rs, (uint32_t)(wave * 32) * row_bytes, row_bytes, lane);
   }
   if (my_q < p.Nq && hf == 0) {
     const float lse = m_run * p.scale + fast_log2(l_tot) * 0.69314718055994531f;
