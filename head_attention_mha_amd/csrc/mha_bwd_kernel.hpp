@@ -63,50 +63,10 @@ constexpr int kBK = 64;            // keys per tile streamed by dq
 constexpr int kBQt = 32;           // queries per tile streamed by dkdv
 constexpr float kLog2e = 1.4426950408889634f;
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// LDS transpose read of 4 x 16-bit values: within each group of 16 lanes,
-// lane i receives element i % 4 of the 8-byte pieces addressed by lanes i/4,
-// 4 + i/4, 8 + i/4 and 12 + i/4.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* ptr) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)ptr));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// 16-byte-chunk swizzle of the tiles that are read both as MFMA rows (16
-// lanes read the 16 rows k_row_order(0..15) at one chunk) and by transpose
-// reads (16 lanes read 4 consecutive rows x 2 chunks, 32 lanes 4 rows x 4
-// chunks). With t = row & 3 and m = (row >> 2) & 3, the 16 rows of a row
-// read get 16 (d = 128) or, per row parity, 8 (d = 64) different chunk
-// positions, and the 4 rows of a transpose read put their chunks on
-// disjoint positions, whether the LDS serves 128 or 256 bytes per pass.
-// (The forward's swizzle, made for row reads only, gives 4-way conflicts on
-// the transpose reads.)
-template <int D>
-__device__ __forceinline__ int t_swz(int row) {
-  const int t = row & 3, m = (row >> 2) & 3;
-  const int gray = m ^ (m >> 1);
-  if constexpr (D == 128) return (4 * t + 2 * (t >> 1)) ^ gray;  // 16 chunks per row
-  else return (2 * t) ^ gray;                                    // 8 chunks per row
-}
-
-// Per-lane byte offsets of the transpose reads that form the A operand
-// "rows = head-dim index 32*db + (lane % 32), k-slots = 8 consecutive tile
-// rows 16*ks + 8*(lane / 32) + 0..7" from a row-major tile whose 16-byte
-// chunks are swizzled by t_swz<D> of the row: two reads per operand, the
-// second 4 rows further (r = 0, 1). Lane (g, a) of 16-lane group g supplies
-// the 8-byte piece of row 8*(g/2) + 4r + a/4 at head-dim index
-// 32*db + 16*(g%2) + 4*(a%4). Everything but these offsets (the 16-row step
-// ks) is an immediate, since the swizzle depends on the row's low 4 bits.
-template <int D>
-__device__ __forceinline__ uint32_t tr_off(int lane, int db, int r) {
-  constexpr int ROWB = 2 * D;
-  const int g = lane >> 4, a = lane & 15;
-  const int row = 8 * (g >> 1) + 4 * r + (a >> 2);
-  const int chunk = 4 * db + 2 * (g & 1) + ((a & 3) >> 1);
-  return row * ROWB + 16 * (chunk ^ t_swz<D>(row)) + 8 * (a & 1);
-}
+using mha::lds_read_tr16;
+using mha::t_swz;
+using mha::tr_off;
+using mha::tr_operand;
 
 // Two packed 16-bit values -> fp32.
 template <typename T>
@@ -123,13 +83,6 @@ __device__ __forceinline__ f32x2 unpack2(uint32_t w) {
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, uint32_t voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)((lds_u8*)lds_dst),
                                            4, voffset, 0, 0, 0);
-}
-
-// The 8 values of one transposed A operand.
-__device__ __forceinline__ u32x4 tr_operand(const uint8_t* base, uint32_t off0, uint32_t off1) {
-  const u32x2 t0 = lds_read_tr16(base + off0);
-  const u32x2 t1 = lds_read_tr16(base + off1);
-  return u32x4{t0[0], t0[1], t1[0], t1[1]};
 }
 
 }  // namespace bwd

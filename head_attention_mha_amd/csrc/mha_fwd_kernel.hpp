@@ -31,7 +31,7 @@
 //   and a softmax phase (VALU), the second group half a period behind the
 //   first: every SIMD holds one wave of each group, so one issues MFMAs
 //   while the other runs its softmax. One workgroup barrier per key tile
-//   (period) covers the reuse of the K and V^T buffers; within a period the
+//   (period) covers the reuse of the K and V buffers; within a period the
 //   groups are not forced into step.
 // * S is computed transposed (keys are MFMA rows, queries are columns), so
 //   each lane owns one query: the row max needs one exchange between lanes
@@ -42,18 +42,17 @@
 //   consecutive keys per 16-key step -- exactly the B-operand fragment of the
 //   P.V product, so P needs no cross-lane layout change ("SparkAttention"
 //   step 3 becomes a register-local conversion).
-// * K tiles are copied global -> LDS by buffer loads that write LDS
+// * K and V tiles are copied global -> LDS by buffer loads that write LDS
 //   directly (no staging registers); rows past the end of the keys read as
 //   zero through the buffer's range check, so the tail needs no branches.
-// * V tiles go through registers (loaded two phases ahead) and are written
-//   transposed into a padded V^T tile, so the V^T operand of the P.V
-//   product is one 16-byte LDS read per MFMA like the K operand.
+//   The V^T operand of the P.V product comes from two LDS transpose reads
+//   (ds_read_b64_tr_b16) of the row-major V tile per MFMA.
 // * The row max is exchanged between the two lane halves with
 //   v_permlane32_swap; barriers are bare s_barrier instructions with the
 //   needed waits made explicit.
 // * LDS tiles are XOR-swizzled in 16-byte units so the MFMA operand reads
-//   are free of bank conflicts; the GEMM phase reads each operand four MFMAs
-//   ahead of its use.
+//   (row reads of K, transpose reads of V) are free of bank conflicts; the
+//   GEMM phase reads each operand four MFMAs ahead of its use.
 // * The O rescale is deferred while a row's max stays within 2^8 (exp2
 //   domain) of the max O and l were last scaled to; O/l and LSE are the same
 //   in exact arithmetic, and the rescale then runs only when the max jumps.
@@ -209,6 +208,58 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
                                            16, voffset, 0, 0, 0);
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS transpose read of 4 x 16-bit values: within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte pieces addressed by lanes i/4,
+// 4 + i/4, 8 + i/4 and 12 + i/4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* ptr) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)ptr));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// 16-byte-chunk swizzle of the tiles that are read both as MFMA rows (16
+// lanes read the 16 rows k_row_order(0..15) at one chunk) and by transpose
+// reads (16 lanes read 4 consecutive rows x 2 chunks, 32 lanes 4 rows x 4
+// chunks). With t = row & 3 and m = (row >> 2) & 3, the 16 rows of a row
+// read get 16 (d = 128) or, per row parity, 8 (d = 64) different chunk
+// positions, and the 4 rows of a transpose read put their chunks on
+// disjoint positions, whether the LDS serves 128 or 256 bytes per pass.
+// (The K tile's swizzle of the forward, made for row reads only, would give
+// 4-way conflicts on the transpose reads.)
+template <int D>
+__device__ __forceinline__ int t_swz(int row) {
+  const int t = row & 3, m = (row >> 2) & 3;
+  const int gray = m ^ (m >> 1);
+  if constexpr (D == 128) return (4 * t + 2 * (t >> 1)) ^ gray;  // 16 chunks per row
+  else return (2 * t) ^ gray;                                    // 8 chunks per row
+}
+
+// Per-lane byte offsets of the transpose reads that form the A operand
+// "rows = head-dim index 32*db + (lane % 32), k-slots = 8 consecutive tile
+// rows 16*ks + 8*(lane / 32) + 0..7" from a row-major tile whose 16-byte
+// chunks are swizzled by t_swz<D> of the row: two reads per operand, the
+// second 4 rows further (r = 0, 1). Lane (g, a) of 16-lane group g supplies
+// the 8-byte piece of row 8*(g/2) + 4r + a/4 at head-dim index
+// 32*db + 16*(g%2) + 4*(a%4). Everything but these offsets (the 16-row step
+// ks) is an immediate, since the swizzle depends on the row's low 4 bits.
+template <int D>
+__device__ __forceinline__ uint32_t tr_off(int lane, int db, int r) {
+  constexpr int ROWB = 2 * D;
+  const int g = lane >> 4, a = lane & 15;
+  const int row = 8 * (g >> 1) + 4 * r + (a >> 2);
+  const int chunk = 4 * db + 2 * (g & 1) + ((a & 3) >> 1);
+  return row * ROWB + 16 * (chunk ^ t_swz<D>(row)) + 8 * (a & 1);
+}
+
+// The 8 values of one transposed A operand.
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* base, uint32_t off0, uint32_t off1) {
+  const u32x2 t0 = lds_read_tr16(base + off0);
+  const u32x2 t1 = lds_read_tr16(base + off1);
+  return u32x4{t0[0], t0[1], t1[0], t1[1]};
+}
+
 // One wave's 32 output rows, held in MFMA-accumulator layout (lane (ln, hf)
 // owns row ln; value r of block db is column 32db + 8(r/4) + 4hf + r%4),
 // scaled by `mul`, rounded to the I/O type and written out through an LDS
@@ -249,7 +300,7 @@ __device__ __forceinline__ void store_rows(const f32x16* acc, float mul, uint8_t
 // n+AHEAD.
 template <int N, int NPV, int NS, int AHEAD>
 struct PinInterleave {
-  static constexpr int reads_of(int) { return 1; }
+  static constexpr int reads_of(int n) { return n < NPV ? 2 : 1; }
   static constexpr int preload() {
     int r = 0;
     for (int n = 0; n < AHEAD; ++n) r += reads_of(n);
@@ -281,22 +332,16 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   constexpr int NCPW = TILEB / 1024 / kWaves;  // 1 KiB copies per wave per tensor
   static_assert(NCPW >= 1, "tile too small for the workgroup");
 
-  // V^T tiles: row d holds the tile's 64 keys of head-dim index d (128
-  // bytes) plus 16 bytes of padding, which keeps both the transposed writes
-  // and the MFMA operand reads free of bank conflicts
-  constexpr int VT_RS = 2 * BK + 16;
-  constexpr int VTB = D * VT_RS;
-  constexpr int VTB_AL = (VTB + 1023) / 1024 * 1024;
   constexpr int OSB = 32 * ROWB;  // one wave's 32 output rows
-  // One LDS allocation laid out by hand: the K and V^T tiles first, so the
+  // One LDS allocation laid out by hand: the K and V tiles first, so the
   // GEMM phases address them with immediate offsets (below 64 KiB), then one
   // output-staging slot per wave for the epilogue.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * TILEB + 2 * VTB_AL + kWaves * OSB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * TILEB + 2 * TILEB + kWaves * OSB];
   uint8_t* const lds_k0 = lds;
   uint8_t* const lds_k1 = lds + TILEB;
-  uint8_t* const lds_vt0 = lds + 2 * TILEB;
-  uint8_t* const lds_vt1 = lds + 2 * TILEB + VTB_AL;
-  uint8_t* const lds_o = lds + 2 * TILEB + 2 * VTB_AL;
+  uint8_t* const lds_v0 = lds + 2 * TILEB;  // V tiles: row-major, chunks swizzled by t_swz
+  uint8_t* const lds_v1 = lds + 2 * TILEB + TILEB;
+  uint8_t* const lds_o = lds + 2 * TILEB + 2 * TILEB;
 
   // ---- work item: (batch, head, query tile) --------------------------------
   // Workgroups are dispatched in index order, round-robin over the 8 XCDs.
@@ -387,31 +432,19 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
 #pragma unroll
     for (int it = 0; it < NCPW; ++it) dma16(r, lk + (it * kWaves + wave) * 1024, k_off[it]);
   };
-  // V goes through registers and is written transposed: lane (kp, dc) of
-  // the copying waves loads rows 2kp and 2kp+1 of the tile at 16-byte chunk
-  // dc and writes, for each of its 8 head-dim indices d = 8dc + i, the word
-  // (V[2kp][d], V[2kp+1][d]) to V^T row d, column kp. Each write instruction
-  // then covers two rows of opposite parity x 32 consecutive words.
-  const bool v_copier = (D == 128) || (wave < 4);
-  const int v_dc = 2 * wave + (lane >> 5);
-  const int v_kp = lane & 31;
-  const uint32_t v_src0 = (uint32_t)(2 * v_kp) * row_bytes + 16 * v_dc;
-  u32x4 vst[2];
-  auto load_v = [&](int j) __attribute__((always_inline)) {
-    if (!v_copier) return;
-    const auto r = rsrc_for(Vb, j);
-    vst[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, v_src0, 0, 0));
-    vst[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, v_src0 + row_bytes, 0, 0));
-  };
-  auto store_v = [&](uint8_t* vt) __attribute__((always_inline)) {
-    if (!v_copier) return;
-    uint8_t* dst = vt + (8 * v_dc) * VT_RS + 4 * v_kp;
+  // V tiles are copied like K, row-major, 16-byte chunks swizzled by
+  // t_swz<D> of the row so the transpose reads of the P.V operand are
+  // conflict-free.
+  uint32_t v_off[NCPW];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t a = vst[0][i >> 1], bb = vst[1][i >> 1];
-      const uint32_t word = (i & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
-      *reinterpret_cast<uint32_t*>(dst + i * VT_RS) = word;
-    }
+  for (int it = 0; it < NCPW; ++it) {
+    const int row = (it * kWaves + wave) * RPI + lane / CH;
+    v_off[it] = row * row_bytes + 16 * ((lane % CH) ^ t_swz<D>(row));
+  }
+  auto issue_v = [&](int j, uint8_t* lv) __attribute__((always_inline)) {
+    const auto r = rsrc_for(Vb, j);
+#pragma unroll
+    for (int it = 0; it < NCPW; ++it) dma16(r, lv + (it * kWaves + wave) * 1024, v_off[it]);
   };
 
   // ---- per-lane LDS read offsets (fixed for the whole kernel) ---------------
@@ -425,9 +458,12 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < DK; ++i) koff[i] = key * ROWB + 16 * ((2 * i + hf) ^ sw);
   }
-  // V^T operand: lane (ln, hf) reads row 32*db + ln, bytes 32*ks + 16*hf
-  // (keys 16*ks + 8*hf .. +7); everything but the lane part is an immediate.
-  const uint32_t vt_off = ln * VT_RS + 16 * hf;
+  // V^T operand: two transpose reads of the row-major V tile per MFMA
+  uint32_t toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) toff[db][r] = tr_off<D>(lane, db, r);
 
   // ---- running state -------------------------------------------------------
   f32x16 o[DB];
@@ -458,8 +494,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // the S^T MFMAs produce a tile nobody reads.
   auto gemm = [&](int j, const uint8_t* lk, const uint8_t* lv) __attribute__((always_inline)) {
     if (j > j_end) return;  // wave-uniform: past this wave's rows
-    uint32_t vo = vt_off, ko[DK];
-    asm volatile("" : "+v"(vo));
+    uint32_t ko[DK];
 #pragma unroll
     for (int i = 0; i < DK; ++i) {
       ko[i] = koff[i];
@@ -471,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       u32x4 a;
       if (n < NPV) {
         const int ks = n / DB, db = n % DB;
-        a = *reinterpret_cast<const u32x4*>(lv + vo + db * 32 * VT_RS + 32 * ks);
+        a = tr_operand(lv + ks * 16 * ROWB, toff[db][0], toff[db][1]);
       } else {
         const int m = n - NPV, i = m / KB, kb = m % KB;
         a = *reinterpret_cast<const u32x4*>(lk + ko[i] + kb * 32 * ROWB);
@@ -573,14 +608,10 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // the other runs its softmax. Each group has its own straight-line loop;
   // the k-th barrier of every wave pairs up. K_j is read in period j, V_j
   // in period j+1.
-  // * At the start of period m every wave starts its share of the LDS copy
-  //   of K_{m+1}, into the K buffer that held K_{m-1} (last read in period
-  //   m-1); it is waited for before barrier #m+1.
-  // * In period m every copying wave writes V_m (already in registers)
-  //   transposed into the V^T buffer that held V_{m-2} (last read in period
-  //   m-1), then starts loading V_{m+1} into the same registers.
-  // Vector-memory loads retire in order, so before barrier #m+1 a wait that
-  // leaves only the two newest loads (V_{m+1}) outstanding covers K_{m+1}.
+  // * At the start of period m every wave starts its share of the LDS
+  //   copies of K_{m+1}, into the K buffer that held K_{m-1}, and of V_m,
+  //   into the V buffer that held V_{m-2} (both last read in period m-1);
+  //   they are waited for before barrier #m+1.
   // Workgroup barrier without a memory fence: __syncthreads() also releases
   // memory at workgroup scope, which would make each wave wait at every
   // barrier for the K copy it started at the beginning of the period. The
@@ -592,55 +623,45 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // K_{m+1} landed and this wave's V^T writes done; V_{m+1} may be in flight.
-  auto wait_k = [&](bool v_in_flight) __attribute__((always_inline)) {
-    if (v_copier && v_in_flight) __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2), lgkmcnt(0)
-    else __builtin_amdgcn_s_waitcnt(0x0070);                           // vmcnt(0), lgkmcnt(0)
+  // K_{m+1} and V_m landed.
+  auto wait_k = [&](bool) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
   };
-  // K_{m+1} copy into K buffer (m+1) & 1; BUF = m & 1 (compile time).
+  // K_{m+1} copy into K buffer (m+1) & 1 and V_m copy into V buffer m & 1;
+  // BUF = m & 1 (compile time).
   auto issue_k_next = [&](int m, auto buf) __attribute__((always_inline)) {
     if constexpr (decltype(buf)::value == 0) {
       if (m + 1 < n_kt) issue_k(m + 1, lds_k1);
+      if (m < n_kt) issue_v(m, lds_v0);
     } else {
       if (m + 1 < n_kt) issue_k(m + 1, lds_k0);
+      if (m < n_kt) issue_v(m, lds_v1);
     }
   };
-  // Write V_m into V^T buffer m & 1 = BUF, then start loading V_{m+1}. The
-  // V_m loads are older than the K_{m+1} copy issued at the start of period m.
-  auto write_v = [&](int m, auto buf) __attribute__((always_inline)) {
-    if (m >= n_kt) return;
-    if (m + 1 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70 | NCPW);  // vmcnt(NCPW)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
-    if constexpr (decltype(buf)::value == 0) store_v(lds_vt0);
-    else store_v(lds_vt1);
-    if (m + 1 < n_kt) load_v(m + 1);
-  };
   // GEMM phase of tile j with BUF = j & 1: K_j in K buffer BUF, V_{j-1} in
-  // V^T buffer BUF ^ 1.
+  // V buffer BUF ^ 1.
   auto gemm_phase = [&](int j, auto buf) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);
     if constexpr (decltype(buf)::value == 0)
-      gemm(j, lds_k0, lds_vt1);
+      gemm(j, lds_k0, lds_v1);
     else
-      gemm(j, lds_k1, lds_vt0);
+      gemm(j, lds_k1, lds_v0);
     __builtin_amdgcn_s_setprio(0);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // the first GEMM phase multiplies P = 0 with V^T buffer 1: make it finite
-  for (int i = tid; i < VTB / 16; i += kThreads)
-    reinterpret_cast<u32x4*>(lds_vt1)[i] = u32x4{0, 0, 0, 0};
+  // the first GEMM phase multiplies P = 0 with V buffer 1: make it finite
+  for (int i = tid; i < TILEB / 16; i += kThreads)
+    reinterpret_cast<u32x4*>(lds_v1)[i] = u32x4{0, 0, 0, 0};
   issue_k(0, lds_k0);
-  load_v(0);
-  wait_k(true);  // K_0 landed; V_0 may be in flight
+  wait_k(true);  // K_0 landed
   barrier();     // #0
   if (grp == 0) {
-    // group A: period j = GEMM(j), write V_j, softmax(j)
+    // group A: period j = GEMM(j), softmax(j)
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
       issue_k_next(j, buf);     // start of period j
       gemm_phase(j, buf);
-      write_v(j, buf);
       softmax(j);
       wait_k(j + 1 < n_kt);
       barrier();                // end of period j
@@ -658,10 +679,9 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     if (j & 1) gemm_phase(j, I1{});
     else gemm_phase(j, I0{});
   } else {
-    // group B: period j = softmax(j-1), write V_j, GEMM(j)
+    // group B: period j = softmax(j-1), GEMM(j)
     issue_k_next(0, I0{});      // start of period 0
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
-      write_v(j, buf);
       gemm_phase(j, buf);
       wait_k(j + 1 < n_kt);
       barrier();                // end of period j
