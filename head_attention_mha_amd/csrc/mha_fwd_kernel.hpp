@@ -389,15 +389,29 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   const int my_q = qw0 + ln;       // query row owned by this lane
 
   // ---- Q fragments (B operand of S^T), read once ---------------------------
+  // The wave's 32 Q rows are copied whole (1 KiB per copy) into its
+  // output-staging slot, which the epilogue only needs later; row r's
+  // 16-byte chunk c lands at chunk c ^ (r mod CH) so the fragment reads
+  // spread over the banks. Rows past Nq read as zero.
   u32x4 qf[DK];
-  if (my_q < p.Nq) {
-    const uint16_t* qrow = Qb + (size_t)my_q * rs + 8 * hf;
+  {
+    constexpr int RPC = 1024 / ROWB;  // rows per copy
+    const int nrows = min(kBQ, p.Nq - q0);
+    const auto r = make_rsrc(Qb + (size_t)q0 * rs, (uint32_t)(nrows - 1) * row_bytes + ROWB);
+    const uint32_t rl = (uint32_t)lane / CH, pc = (uint32_t)lane % CH;
 #pragma unroll
-    for (int i = 0; i < DK; ++i) qf[i] = *reinterpret_cast<const u32x4*>(qrow + 16 * i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < DK; ++i) qf[i] = u32x4{0, 0, 0, 0};
+    for (int c = 0; c < OSB / 1024; ++c) {
+      const uint32_t row = (uint32_t)(c * RPC) + rl;  // row within the wave's 32
+      dma16(r, lds_o + wave * OSB + c * 1024,
+            (uint32_t)(wave * 32 + row) * row_bytes + 16 * ((pc ^ row) & (CH - 1)));
+    }
   }
+  auto read_q = [&]() __attribute__((always_inline)) {
+    const uint8_t* qs = lds_o + wave * OSB + ln * ROWB;
+#pragma unroll
+    for (int i = 0; i < DK; ++i)
+      qf[i] = *reinterpret_cast<const u32x4*>(qs + 16 * ((2 * i + hf) ^ (ln & (CH - 1))));
+  };
 
   // ---- key tiles this query tile needs -------------------------------------
   const int n_ktiles_all = (p.Nk + BK - 1) / BK;
@@ -655,7 +669,8 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   for (int i = tid; i < TILEB / 16; i += kThreads)
     reinterpret_cast<u32x4*>(lds_v1)[i] = u32x4{0, 0, 0, 0};
   issue_k(0, lds_k0);
-  wait_k(true);  // K_0 landed
+  wait_k(true);  // Q and K_0 landed
+  read_q();
   barrier();     // #0
   if (grp == 0) {
     // group A: period j = GEMM(j), softmax(j)
