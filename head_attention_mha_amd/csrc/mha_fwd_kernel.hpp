@@ -208,6 +208,21 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst
                                            16, voffset, 0, 0, 0);
 }
 
+// The same copy issued by inline asm: the compiler then does not treat it as
+// an LDS write and adds no wait for it before later LDS reads (it cannot
+// tell the buffer being filled from the ones being read, so it would wait
+// for every copy in flight). Code that uses it waits explicitly (vmcnt) and
+// passes a barrier before reading what it copied.
+__device__ __forceinline__ void dma16_async(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds_dst);
+  // M0 holds the LDS address; s_nop: the copy may not read M0 in the cycle
+  // after it was written
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(r), "{m0}"(m0)
+               : "memory");
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -306,8 +321,11 @@ struct PinInterleave {
     for (int n = 0; n < AHEAD; ++n) r += reads_of(n);
     return r;
   }
+  // region before the first MFMA: the first operand reads
+  static __device__ __forceinline__ void pin_preload() {
+    __builtin_amdgcn_sched_group_barrier(0x100, preload(), 0);
+  }
   static __device__ __forceinline__ void apply() {
-    if constexpr (N == 0) __builtin_amdgcn_sched_group_barrier(0x100, preload(), 0);
     if constexpr (N < NPV + NS) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if constexpr (N + AHEAD < NPV + NS)
@@ -436,15 +454,16 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     const int pc = lane % CH;  // physical chunk in LDS
     k_off[it] = row * row_bytes + 16 * (pc ^ k_swz<D>(row));
   }
+  // A tile j >= n_kt gets an empty range: its copies read nothing.
   auto rsrc_for = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
     const int kbase = j * BK;
     const int nvalid = min(BK, p.Nk - kbase);
-    return make_rsrc(base + (size_t)kbase * rs, (uint32_t)(nvalid - 1) * row_bytes + ROWB);
+    return make_rsrc(base + (size_t)kbase * rs, j < n_kt ? (uint32_t)(nvalid - 1) * row_bytes + ROWB : 0u);
   };
   auto issue_k = [&](int j, uint8_t* lk) __attribute__((always_inline)) {
     const auto r = rsrc_for(Kb, j);
 #pragma unroll
-    for (int it = 0; it < NCPW; ++it) dma16(r, lk + (it * kWaves + wave) * 1024, k_off[it]);
+    for (int it = 0; it < NCPW; ++it) dma16_async(r, lk + (it * kWaves + wave) * 1024, k_off[it]);
   };
   // V tiles are copied like K, row-major, 16-byte chunks swizzled by
   // t_swz<D> of the row so the transpose reads of the P.V operand are
@@ -458,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   auto issue_v = [&](int j, uint8_t* lv) __attribute__((always_inline)) {
     const auto r = rsrc_for(Vb, j);
 #pragma unroll
-    for (int it = 0; it < NCPW; ++it) dma16(r, lv + (it * kWaves + wave) * 1024, v_off[it]);
+    for (int it = 0; it < NCPW; ++it) dma16_async(r, lv + (it * kWaves + wave) * 1024, v_off[it]);
   };
 
   // ---- per-lane LDS read offsets (fixed for the whole kernel) ---------------
@@ -506,8 +525,9 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // their own registers and copy it across on every tile): for j = 0 the
   // P.V MFMAs multiply P = 0 with a zero-filled V buffer, and for j = j_end
   // the S^T MFMAs produce a tile nobody reads.
-  auto gemm = [&](int j, const uint8_t* lk, const uint8_t* lv) __attribute__((always_inline)) {
-    if (j > j_end) return;  // wave-uniform: past this wave's rows
+  // `copies` issues this wave's tile copies right after the first operand
+  // reads (their latency hides the issue) and before the first MFMA.
+  auto gemm = [&](int j, const uint8_t* lk, const uint8_t* lv, auto copies) __attribute__((always_inline)) {
     uint32_t ko[DK];
 #pragma unroll
     for (int i = 0; i < DK; ++i) {
@@ -527,13 +547,18 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       }
       return a;
     };
+    // the first operand reads and the copies go out on every wave (a wave
+    // past its rows discards the operands), so the copies appear once
+    u32x4 buf[kAhead];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) buf[n] = load_op(n);
+    copies();
+    PinInterleave<0, NPV, NS, kAhead>::pin_preload();
+    if (j > j_end) return;  // wave-uniform: past this wave's rows
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    u32x4 buf[kAhead];
-#pragma unroll
-    for (int n = 0; n < kAhead; ++n) buf[n] = load_op(n);
 #pragma unroll
     for (int n = 0; n < NPV + NS; ++n) {
       const u32x4 a = buf[n % kAhead];
@@ -546,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
         s[kb] = O_::mfma(a, qf[i], s[kb]);
       }
     }
-    // pin the order: the preloads, then per MFMA the reads kAhead ahead
+    // pin the order: per MFMA the reads kAhead ahead
     PinInterleave<0, NPV, NS, kAhead>::apply();
   };
 
@@ -652,14 +677,26 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       if (m < n_kt) issue_v(m, lds_v1);
     }
   };
+  // The same for m < n_kt without a branch, so that it can sit inside a GEMM
+  // phase: for m + 1 = n_kt the K copy has an empty range and reads nothing.
+  auto issue_k_next_inline = [&](int m, auto buf) __attribute__((always_inline)) {
+    if constexpr (decltype(buf)::value == 0) {
+      issue_k(m + 1, lds_k1);
+      issue_v(m, lds_v0);
+    } else {
+      issue_k(m + 1, lds_k0);
+      issue_v(m, lds_v1);
+    }
+  };
+  auto no_copies = []() __attribute__((always_inline)) {};
   // GEMM phase of tile j with BUF = j & 1: K_j in K buffer BUF, V_{j-1} in
   // V buffer BUF ^ 1.
-  auto gemm_phase = [&](int j, auto buf) __attribute__((always_inline)) {
+  auto gemm_phase = [&](int j, auto buf, auto copies) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);
     if constexpr (decltype(buf)::value == 0)
-      gemm(j, lds_k0, lds_v1);
+      gemm(j, lds_k0, lds_v1, copies);
     else
-      gemm(j, lds_k1, lds_v0);
+      gemm(j, lds_k1, lds_v0, copies);
     __builtin_amdgcn_s_setprio(0);
   };
   using I0 = std::integral_constant<int, 0>;
@@ -675,8 +712,8 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   if (grp == 0) {
     // group A: period j = GEMM(j), softmax(j)
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
-      issue_k_next(j, buf);     // start of period j
-      gemm_phase(j, buf);
+      // start of period j: the copies go out inside the GEMM phase
+      gemm_phase(j, buf, [&]() __attribute__((always_inline)) { issue_k_next_inline(j, buf); });
       softmax(j);
       wait_k(j + 1 < n_kt);
       barrier();                // end of period j
@@ -691,13 +728,13 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       ++j;
     }
     // P.V of the last tile
-    if (j & 1) gemm_phase(j, I1{});
-    else gemm_phase(j, I0{});
+    if (j & 1) gemm_phase(j, I1{}, no_copies);
+    else gemm_phase(j, I0{}, no_copies);
   } else {
     // group B: period j = softmax(j-1), GEMM(j)
     issue_k_next(0, I0{});      // start of period 0
     auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
-      gemm_phase(j, buf);
+      gemm_phase(j, buf, no_copies);
       wait_k(j + 1 < n_kt);
       barrier();                // end of period j
       if constexpr (decltype(buf)::value == 0)
@@ -716,8 +753,8 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       ++j;
     }
     // P.V of the last tile
-    if (j & 1) gemm_phase(j, I1{});
-    else gemm_phase(j, I0{});
+    if (j & 1) gemm_phase(j, I1{}, no_copies);
+    else gemm_phase(j, I0{}, no_copies);
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale*m + ln(l) ------------------------
