@@ -647,10 +647,11 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // the other runs its softmax. Each group has its own straight-line loop;
   // the k-th barrier of every wave pairs up. K_j is read in period j, V_j
   // in period j+1.
-  // * At the start of period m every wave starts its share of the LDS
-  //   copies of K_{m+1}, into the K buffer that held K_{m-1}, and of V_m,
-  //   into the V buffer that held V_{m-2} (both last read in period m-1);
-  //   they are waited for before barrier #m+1.
+  // * Early in period m every wave starts its share of the LDS copies of
+  //   K_{m+1}, into the K buffer that held K_{m-1}, and of V_m, into the V
+  //   buffer that held V_{m-2} (both last read in period m-1): group B right
+  //   after barrier #m, group A inside its GEMM phase, after its first
+  //   operand reads. They are waited for before barrier #m+1.
   // Workgroup barrier without a memory fence: __syncthreads() also releases
   // memory at workgroup scope, which would make each wave wait at every
   // barrier for the K copy it started at the beginning of the period. The
