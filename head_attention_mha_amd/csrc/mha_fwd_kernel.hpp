@@ -52,7 +52,7 @@
 //   needed waits made explicit.
 // * LDS tiles are XOR-swizzled in 16-byte units so the MFMA operand reads
 //   (row reads of K, transpose reads of V) are free of bank conflicts; the
-//   GEMM phase reads each operand four MFMAs ahead of its use.
+//   GEMM phase reads each operand three MFMAs ahead of its use.
 // * The O rescale is deferred while a row's max stays within 2^8 (exp2
 //   domain) of the max O and l were last scaled to; O/l and LSE are the same
 //   in exact arithmetic, and the rescale then runs only when the max jumps.
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // immediate offset) instead of hoisting one register per (buffer, step).
   constexpr int NPV = PK * DB;  // P.V MFMAs per tile
   constexpr int NS = DK * KB;   // S^T MFMAs per tile
-  constexpr int kAhead = 4;
+  constexpr int kAhead = 3;
   // One code path for every GEMM phase (distinct paths would each keep O in
   // their own registers and copy it across on every tile): for j = 0 the
   // P.V MFMAs multiply P = 0 with a zero-filled V buffer, and for j = j_end
