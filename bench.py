@@ -13,13 +13,16 @@ regime of the FlashAttention long-sequence post). Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import re
 import json
 import math
 import os
+import resource
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -33,6 +36,8 @@ METRIC_BWD = ("attention bwd TFLOP/s (5-matmul count 10*B*H*Nq*Nk*d, halved caus
               "MFMA bf16 peak")
 PEAK_TFLOPS = 2500.0  # MI355X published dense bf16/fp16 MFMA peak
 PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
+MFMA_FLOP_PER_CLK_PER_CU = 4096  # dense bf16/fp16 MFMA work per CU per cycle (gfx950)
+MALL_FLUSH_MIB = 1024  # larger than the 256 MB last-level (MALL) cache
 METRIC_KL = ("attention KL(P1||P2) forward TFLOP/s (two QK^T products, 4*B*H*Nq*Nk*d, halved "
              "causal) and % of MFMA bf16 peak")
 METRIC_PROJ = ("output projection (head concat then O W^T + b) TFLOP/s, 2*B*Nq*H*d*E, and % of "
@@ -41,18 +46,18 @@ METRIC_SPLIT = ("attention decode forward (split over keys) HBM GB/s: Q, K, V re
                 "written once, per second")
 _CSRC = os.path.join(ROOT, "head_attention_mha_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
-                  ("mha_common.hpp", "mha_fwd_kernel.hpp", "mha_fwd.hip")]
+                  ("mha_common.hpp", "mha_tiles.hpp", "mha_fwd_kernel.hpp", "mha_fwd.hip")]
 KERNEL_SOURCES_SPLIT = [os.path.join(_CSRC, f) for f in
-                        ("mha_common.hpp", "mha_fwd_kernel.hpp", "mha_split_kernel.hpp",
+                        ("mha_common.hpp", "mha_tiles.hpp", "mha_fwd_kernel.hpp", "mha_split_kernel.hpp",
                          "mha_splitkv.hip")]
 KERNEL_SOURCES_BWD = [os.path.join(_CSRC, f) for f in
-                      ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp",
+                      ("mha_common.hpp", "mha_tiles.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp",
                        "mha_bwd_kernel.hpp", "mha_bwd.hip")]
 KERNEL_SOURCES_PROJ = [os.path.join(_CSRC, f) for f in
-                       ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp",
+                       ("mha_common.hpp", "mha_tiles.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp",
                         "mha_proj_kernel.hpp", "mha_proj.hip")]
 KERNEL_SOURCES_KL = [os.path.join(_CSRC, f) for f in
-                     ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp", "mha_kl_kernel.hpp",
+                     ("mha_common.hpp", "mha_tiles.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp", "mha_kl_kernel.hpp",
                       "mha_kl.hip")]
 
 
@@ -68,26 +73,82 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def hbm_traffic(workload: str, which: str = "fwd"):
-    """Per-launch HBM bytes (FETCH + WRITE) from the committed counter summary,
-    or None when there is none or the kernel sources changed since."""
-    name = f"hbm_traffic_{workload}.txt" if which == "fwd" else f"hbm_traffic_{which}_{workload}.txt"
+def profile_fields(kind: str, workload: str, which: str = "fwd"):
+    """Fields of a committed counter summary (``profiles/<kind>_[<pass>_]<workload>.txt``,
+    ``key: value`` lines), or None when there is none or the kernel sources
+    changed since the counters were taken."""
+    name = f"{kind}_{workload}.txt" if which == "fwd" else f"{kind}_{which}_{workload}.txt"
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
-        if ":" in line:
+        if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT,
             "kl": KERNEL_SOURCES_KL, "proj": KERNEL_SOURCES_PROJ}[which]
     if fields.get("kernel_source_sha256_16") != kernel_source_hash(srcs):
         return None
+    return fields
+
+
+def _float(fields, key):
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[key]) if fields else None
     except (KeyError, ValueError):
         return None
+
+
+def hbm_traffic(workload: str, which: str = "fwd"):
+    """Per-launch HBM bytes (FETCH + WRITE) from the committed counter summary,
+    or None when there is none or the kernel sources changed since."""
+    return _float(profile_fields("hbm_traffic", workload, which), "hbm_bytes_per_launch")
+
+
+def sq_counters(workload: str, which: str = "fwd") -> dict:
+    """MFMA busy fraction and the engine clock under load from the committed
+    SQ/GRBM counter summary (None where it is missing or stale)."""
+    f = profile_fields("sq_counters", workload, which)
+    return {"mfma_busy": _float(f, "mfma_busy_frac"),
+            "sclk_mhz_under_load": _float(f, "grbm_sclk_mhz")}
+
+
+def device_info(torch) -> dict:
+    """CU count and peak engine clock of device 0 (hipDeviceGetAttribute) and
+    the dense bf16/fp16 MFMA peak they give: CUs x clock x 4096 FLOP/clk."""
+    props = torch.cuda.get_device_properties(0)
+    cus, khz = int(props.multi_processor_count), None
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        val = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0:  # hipDeviceAttributeClockRate
+            khz = val.value
+    except OSError:  # pragma: no cover
+        pass
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": cus,
+            "max_sclk_mhz": khz / 1000.0 if khz else None}
+    info["peak_tflops_from_device"] = (round(cus * khz * 1e3 * MFMA_FLOP_PER_CLK_PER_CU / 1e12, 1)
+                                       if khz else None)
+    return info
+
+
+def cpu_workers() -> tuple[int, int]:
+    """(workers, CPUs in this process's affinity set): one worker per CPU,
+    capped by OMP_NUM_THREADS (the host's share of CPUs per GPU) when set."""
+    aff = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS") or aff)
+    return max(1, min(aff, cap)), aff
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def to_device(torch, bits, dtype):
@@ -95,155 +156,199 @@ def to_device(torch, bits, dtype):
     return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
 
 
-def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float) -> dict:
-    """The fp64 oracle, as it stands, on evenly spaced query rows of every head."""
+def run_pool(thunks):
+    """Run the oracle calls ``thunks`` on a pool of threads, one per worker
+    CPU, each with BLAS pinned to one thread (NumPy releases the GIL inside
+    its matrix products and array loops). Returns (results, seconds,
+    workers)."""
+    from threadpoolctl import threadpool_limits
+    workers, _ = cpu_workers()
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            out = list(ex.map(lambda f: f(), thunks))
+        t = time.perf_counter() - t0
+    return out, t, min(workers, max(1, len(thunks)))
+
+
+def _host_fields(workers: int) -> dict:
+    _, aff = cpu_workers()
+    return {"cores": workers, "affinity_cpus": aff, "cpu_model": cpu_model(),
+            "blas_threads_per_worker": 1,
+            "peak_rss_gib": round(resource.getrusage(resource.RUSAGE_SELF).ru_maxrss / 2**20, 2)}
+
+
+def _row_tasks(fn, B, H, rows, chunk=2048):
+    """One oracle call per (b, h, chunk of rows); returns thunks and keys."""
+    thunks, keys = [], []
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, len(rows), chunk):
+                r = rows[r0:r0 + chunk]
+                thunks.append(lambda b=b, h=h, r=r: fn(b, h, r))
+                keys.append((b, h, r0, len(r)))
+    return thunks, keys
+
+
+def _sized_run(one, w, target_s: float):
+    """Runs ``one`` over evenly spaced rows of every (b, h), growing the row
+    count from 16 until a run takes at least a third of ``target_s`` or
+    covers every row; returns that run (rows, thunks, keys, results,
+    seconds, workers)."""
+    n = 16
+    while True:
+        rows = np.unique(np.linspace(0, w.Nq - 1, min(n, w.Nq)).astype(np.int64))
+        thunks, keys = _row_tasks(one, w.B, w.H, rows)
+        res, t, workers = run_pool(thunks)
+        if len(rows) >= w.Nq or t >= target_s / 3:
+            return rows, thunks, keys, res, t, workers
+        n = int(len(rows) * min(8.0, max(1.5, target_s / max(t, 1e-6))))
+
+
+def cpu_baseline(w: wl.Workload, qb, kb, vb, target_s: float, gpu=None) -> dict:
+    """The fp64 oracle, as it stands, on evenly spaced query rows of every
+    (batch, head), one call per (b, h, chunk of rows) on a pool of worker
+    threads. With ``gpu`` = (O bits, LSE) of the GPU run, the same oracle
+    results also give the parity line for the rows timed."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
-                      if i.get("user_api") == "blas") or 1
-    except Exception:  # pragma: no cover
-        threads = 1
     q, k, v = (wl.bits_to_f64(x, w.dtype) for x in (qb, kb, vb))
 
-    def timed(rows):
-        t0 = time.perf_counter()
-        oracle.attention_fwd(q, k, v, w.causal, w.scale, rows=rows)
-        return time.perf_counter() - t0
+    def one(b, h, r):
+        return oracle.attention_fwd(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1],
+                                    v[b:b + 1, :, h:h + 1], w.causal, w.scale, rows=r)
 
-    pilot = np.unique(np.linspace(0, w.Nq - 1, 16).astype(np.int64))
-    t_p = max(timed(pilot), 1e-6)
-    n = int(min(w.Nq, max(16, len(pilot) * target_s / t_p)))
-    rows = np.unique(np.linspace(0, w.Nq - 1, n).astype(np.int64))
-    t = timed(rows)
+    rows, thunks, keys, res, t, workers = _sized_run(one, w, target_s)
     vis = (rows + 1).clip(max=w.Nk) if w.causal else np.full(len(rows), w.Nk)
     flops = 4.0 * w.d * float(vis.sum()) * w.B * w.H
-    return {
+    own = 4.0 * w.d * w.Nk * len(rows) * w.B * w.H  # the oracle forms every score, then masks
+    out = {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        **_host_fields(workers),
         "kind": "oracle",
-        "sample": (f"{len(rows)} evenly spaced query rows of each of the {w.B * w.H} heads "
-                   f"({len(rows) / w.Nq:.1%} of the rows, all their keys), fp64 NumPy, "
-                   f"{t:.1f} s; FLOPs counted as 4*d*visible keys per row"),
+        "sample": (f"{len(rows)} evenly spaced query rows of each of the {w.B * w.H} (batch, head) "
+                   f"pairs ({len(rows) / w.Nq:.1%} of the rows, all their keys), fp64 NumPy, "
+                   f"{len(thunks)} calls of <= 2048 rows on {workers} worker threads, {t:.1f} s; "
+                   f"FLOPs counted as 4*d*visible keys per row"),
         "seconds": t,
+        "oracle_own_tflops": own / t / 1e12,
     }
+    if gpu is not None:
+        from parity import compare, report  # tests/parity.py: the comparison rule
+        O_ref = np.empty((w.B, len(rows), w.H, w.d))
+        L_ref = np.empty((w.B, w.H, len(rows)))
+        for (b, h, r0, n), (O, L) in zip(keys, res):
+            O_ref[b, r0:r0 + n, h] = O[0, :, 0]
+            L_ref[b, h, r0:r0 + n] = L[0, 0]
+        o_bits, lse = gpu
+        st = compare(o_bits[:, rows], lse[:, :, rows], O_ref, L_ref, w.dtype, rows=rows)
+        out["parity"] = {"line": report(st, w.name), "o_max_abs": st["o_max"],
+                         "o_max_at": st["o_max_at"], "o_mean_abs": st["o_mean"],
+                         "floor": st["floor"], "floor_at": st["floor_at"],
+                         "o_n_over_1e-2": st["o_n_over"], "lse_max_abs": st["lse_max"],
+                         "rows_compared": int(len(rows)), "finite": st["finite"]}
+    return out
 
 
 def cpu_baseline_kl(w: wl.Workload, q1b, k1b, q2b, k2b, target_s: float) -> dict:
     """The fp64 KL oracle, as it stands, on evenly spaced query rows of every
-    head (all keys), sized to about ``target_s``."""
+    (batch, head) (all keys), one call per (b, h, chunk of rows) on the pool."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
-                      if i.get("user_api") == "blas") or 1
-    except Exception:  # pragma: no cover
-        threads = 1
     x = [wl.bits_to_f64(a, w.dtype) for a in (q1b, k1b, q2b, k2b)]
 
-    def timed(rows):
-        t0 = time.perf_counter()
-        oracle.attention_kl(*x, w.causal, w.scale, rows=rows)
-        return time.perf_counter() - t0
+    def one(b, h, r):
+        return oracle.attention_kl(*(a[b:b + 1, :, h:h + 1] for a in x), w.causal, w.scale, rows=r)
 
-    pilot = np.unique(np.linspace(0, w.Nq - 1, 16).astype(np.int64))
-    t_p = max(timed(pilot), 1e-6)
-    n = int(min(w.Nq, max(16, len(pilot) * target_s / t_p)))
-    rows = np.unique(np.linspace(0, w.Nq - 1, n).astype(np.int64))
-    t = timed(rows)
+    rows, thunks, _, _, t, workers = _sized_run(one, w, target_s)
     vis = (rows + 1).clip(max=w.Nk) if w.causal else np.full(len(rows), w.Nk)
     flops = 4.0 * w.d * float(vis.sum()) * w.B * w.H
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        **_host_fields(workers),
         "kind": "oracle",
-        "sample": (f"{len(rows)} evenly spaced query rows of each of the {w.B * w.H} heads "
-                   f"({len(rows) / w.Nq:.1%} of the rows, all their keys), fp64 NumPy, "
-                   f"{t:.1f} s; FLOPs counted as 4*d*visible keys per row"),
+        "sample": (f"{len(rows)} evenly spaced query rows of each of the {w.B * w.H} (batch, head) "
+                   f"pairs ({len(rows) / w.Nq:.1%} of the rows, all their keys), fp64 NumPy, "
+                   f"{len(thunks)} calls on {workers} worker threads, {t:.1f} s; FLOPs counted as "
+                   f"4*d*visible keys per row"),
         "seconds": t,
     }
 
 
 def cpu_baseline_split(w: wl.Workload, qb, kb, vb, target_s: float) -> dict:
-    """The fp64 split-over-keys oracle, as it stands, on whole batch entries
-    of the workload (all their heads), doubling their number until the run
-    takes about a quarter of ``target_s`` or covers the workload."""
+    """The fp64 split-over-keys oracle, as it stands, one call per (batch
+    entry, head) on the pool, over whole batch entries, doubling their number
+    until the run takes about a quarter of ``target_s`` or covers the
+    workload."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
-                      if i.get("user_api") == "blas") or 1
-    except Exception:  # pragma: no cover
-        threads = 1
     n_splits = max(1, min(256, -(-w.Nk // 2048)))
     bounds = np.linspace(0, w.Nk, n_splits + 1).astype(np.int64)
+    q, k, v = (wl.bits_to_f64(x, w.dtype) for x in (qb, kb, vb))
 
     def timed(nb):
-        q, k, v = (wl.bits_to_f64(x[:nb], w.dtype) for x in (qb, kb, vb))
-        t0 = time.perf_counter()
-        oracle.attention_fwd_split(q, k, v, w.causal, w.scale, bounds)
-        return time.perf_counter() - t0
+        thunks = [lambda b=b, h=h: oracle.attention_fwd_split(
+            q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1], v[b:b + 1, :, h:h + 1],
+            w.causal, w.scale, bounds) for b in range(nb) for h in range(w.H)]
+        _, t, workers = run_pool(thunks)
+        return t, workers
 
     nb = 1
-    t = timed(nb)
+    t, workers = timed(nb)
     while nb < w.B and t < target_s / 4:
         nb = min(w.B, 2 * nb)
-        t = timed(nb)
+        t, workers = timed(nb)
     bytes_ = nb * w.H * ((2 * w.Nq + 2 * w.Nk) * w.d * 2 + 4 * w.Nq)
     return {
         "value": bytes_ / t / 1e9,
         "unit": "GB/s",
-        "cores": threads,
+        **_host_fields(workers),
         "kind": "oracle",
         "sample": (f"batch entries 0..{nb - 1} ({nb} of {w.B}, all {w.H} heads), {n_splits} key "
-                   f"splits, fp64 NumPy, {t:.2f} s; bytes counted as for the GPU line"),
+                   f"splits, fp64 NumPy, one call per (b, h) on {workers} worker threads, "
+                   f"{t:.2f} s; bytes counted as for the GPU line"),
         "seconds": t,
     }
 
 
 def cpu_baseline_bwd(w: wl.Workload, qb, kb, vb, gb, target_s: float) -> dict:
-    """The fp64 backward oracle, as it stands, on a bounded sample.
+    """The fp64 backward oracle, as it stands, on a bounded sample, one call
+    per head on the pool.
 
     The sample is the first n tokens (queries and keys) of the first m heads
     of batch entry 0: a prefix of a sequence is a complete problem of the
-    same kind (causal stays causal). n grows until one head takes about a
-    quarter of ``target_s`` or covers the whole sequence; then whole heads
-    are added while the time stays within ``target_s``."""
+    same kind (causal stays causal). n grows until the heads take about a
+    quarter of ``target_s`` or cover the whole sequence; then more heads are
+    added while the time stays within ``target_s``."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
-                      if i.get("user_api") == "blas") or 1
-    except Exception:  # pragma: no cover
-        threads = 1
     q, k, v, do = (wl.bits_to_f64(x[:1], w.dtype) for x in (qb, kb, vb, gb))
+    workers, _ = cpu_workers()
 
     def timed(n, m):
         nk = n if w.Nq == w.Nk else w.Nk
-        t0 = time.perf_counter()
-        oracle.attention_bwd(q[:, :n, :m], k[:, :nk, :m], v[:, :nk, :m], do[:, :n, :m],
-                             w.causal, w.scale)
-        return time.perf_counter() - t0, nk
+        thunks = [lambda h=h: oracle.attention_bwd(
+            q[:, :n, h:h + 1], k[:, :nk, h:h + 1], v[:, :nk, h:h + 1], do[:, :n, h:h + 1],
+            w.causal, w.scale) for h in range(m)]
+        _, t, used = run_pool(thunks)
+        return t, nk, used
 
-    n, m = min(w.Nq, 256), 1
-    t, nk = timed(n, m)
+    m = min(w.H, workers)
+    n = min(w.Nq, 256)
+    t, nk, used = timed(n, m)
     while n < w.Nq and t < target_s / 4:
         n = min(w.Nq, int(n * 1.6))
-        t, nk = timed(n, m)
-    if n == w.Nq and w.H > 1:
-        m = int(max(1, min(w.H, target_s / max(t, 1e-6))))
-        if m > 1:
-            t, nk = timed(n, m)
+        t, nk, used = timed(n, m)
+    if n == w.Nq and w.H > m and t < target_s / 2:
+        m = int(max(m, min(w.H, m * target_s / max(t, 1e-6))))
+        t, nk, used = timed(n, m)
     flops = 10.0 * n * nk * w.d * m / (2.0 if w.causal else 1.0)
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        **_host_fields(used),
         "kind": "oracle",
         "sample": (f"the first {n} queries and {nk} keys of heads 0..{m - 1} of batch entry 0, "
-                   f"fp64 NumPy, {t:.1f} s; FLOPs counted as for the GPU line"),
+                   f"fp64 NumPy, one call per head on {used} worker threads, {t:.1f} s; FLOPs "
+                   f"counted as for the GPU line"),
         "seconds": t,
     }
 
@@ -296,7 +401,8 @@ def bench_proj(args, torch, mha, w) -> int:
     tflops = w.flops / (ms * 1e-3) / 1e12
     achieved = w.flops / (per.mean() * 1e-3) / 1e12
     line = {
-        "metric": METRIC_PROJ, "value": round(tflops, 2), "unit": "TFLOP/s",
+        "metric": f"{METRIC_PROJ} (B={w.B},Nq={w.Nq},H={w.H},d={w.d},E={w.E}, {w.dtype})",
+        "value": round(tflops, 2), "unit": "TFLOP/s",
         "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2), "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
@@ -310,7 +416,7 @@ def bench_proj(args, torch, mha, w) -> int:
                                    "min": round(float(per.min()), 5)}},
         "timed_wall_s": round(wall, 3),
         "kernel_source_sha256_16": kernel_source_hash(KERNEL_SOURCES_PROJ),
-        "device": torch.cuda.get_device_name(0),
+        "device": device_info(torch),
     }
     if not args.no_cpu_baseline:
         print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
@@ -323,31 +429,27 @@ def bench_proj(args, torch, mha, w) -> int:
 
 
 def cpu_baseline_proj(w, ob, wb, bb, target_s: float) -> dict:
-    """The fp64 projection oracle, as it stands, on leading token rows."""
+    """The fp64 projection oracle, as it stands, on leading token rows, one
+    call per chunk of 256 rows on the pool."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = sum(int(i.get("num_threads", 1)) for i in threadpool_info()
-                      if i.get("user_api") == "blas") or 1
-    except Exception:  # pragma: no cover
-        threads = 1
     wt, b = wl.bits_to_f64(wb, w.dtype), wl.bits_to_f64(bb, w.dtype)
     x = ob.reshape(w.B * w.Nq, w.H, w.d)
 
     def timed(n):
-        o = wl.bits_to_f64(x[:n], w.dtype)[None]
-        t0 = time.perf_counter()
-        oracle.out_proj(o, wt, b)
-        return time.perf_counter() - t0
+        xs = wl.bits_to_f64(x[:n], w.dtype)
+        thunks = [lambda r=r: oracle.out_proj(xs[None, r:r + 256], wt, b) for r in range(0, n, 256)]
+        _, t, used = run_pool(thunks)
+        return t, used
 
-    n = min(w.B * w.Nq, 256)
-    t = timed(n)
+    n = min(w.B * w.Nq, 1024)
+    t, used = timed(n)
     while n < w.B * w.Nq and t < target_s / 4:
         n = min(w.B * w.Nq, 2 * n)
-        t = timed(n)
+        t, used = timed(n)
     flops = 2.0 * n * w.H * w.d * w.E
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"the first {n} of {w.B * w.Nq} token rows, fp64 NumPy matmul, {t:.2f} s"),
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", **_host_fields(used), "kind": "oracle",
+            "sample": (f"the first {n} of {w.B * w.Nq} token rows, fp64 NumPy matmul, chunks of "
+                       f"256 rows on {used} worker threads, {t:.2f} s"),
             "seconds": t}
 
 
@@ -475,18 +577,47 @@ def main() -> int:
     total_ms = ev[0].elapsed_time(ev[K])
     ms_per_step = total_ms / K
 
+    # outside the timed region: the same launches back to back with one event
+    # pair around them (amortised, no event between launches), and launches
+    # each preceded by a write of MALL_FLUSH_MIB MiB (the inputs then come
+    # from HBM, not from the last-level cache)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    amortised_ms = e0.elapsed_time(e1) / K
+    flushed_ms = None
+    if args.which == "fwd":
+        scratch = torch.empty(MALL_FLUSH_MIB << 18, dtype=torch.float32, device=q.device)
+        fl = []
+        for _ in range(min(K, 20)):
+            scratch.fill_(1.0)
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            fl.append(a.elapsed_time(b_))
+        flushed_ms = float(np.median(fl))
+        del scratch
+
+    dev = device_info(torch)
     flops = 2.5 * w.flops if args.which == "bwd" else w.flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (per.mean() * 1e-3) / 1e12
     traffic = hbm_traffic(w.name, args.which)
     srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT,
             "kl": KERNEL_SOURCES_KL}
+    shape = (f"B={w.B},H={w.H},Nq={w.Nq},Nk={w.Nk},d={w.d}{' causal' if w.causal else ''}, "
+             f"{w.dtype}")
     if args.which == "splitkv":
         # HBM-bound: the metric is the algorithmic bytes moved per second
         gbs = w.io_bytes / (ms_per_step * 1e-3) / 1e9
         gbs_launch = w.io_bytes / (per.mean() * 1e-3) / 1e9
         line = {
-            "metric": METRIC_SPLIT,
+            "metric": f"{METRIC_SPLIT} ({shape})",
             "value": round(gbs, 1),
             "unit": "GB/s",
             "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
@@ -497,19 +628,41 @@ def main() -> int:
                 "kernel": "mha_fwd_splitkv (partial and merge kernels, one call)",
                 "bytes_per_step": w.io_bytes, "n_splits": n_splits}
     else:
+        metric = {"fwd": METRIC, "bwd": METRIC_BWD, "kl": METRIC_KL}[args.which]
+        if args.which == "fwd" and w.name != "long_causal":
+            metric = f"attention fwd TFLOP/s and % of MFMA bf16 peak ({shape})"
+        elif args.which != "fwd":
+            metric = f"{metric} ({shape})"
         line = {
-            "metric": {"fwd": METRIC, "bwd": METRIC_BWD, "kl": METRIC_KL}[args.which],
+            "metric": metric,
             "value": round(tflops, 2),
             "unit": "TFLOP/s",
             "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
         }
+        io_bytes = w.io_bytes if args.which == "fwd" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel": {"fwd": "mha_fwd_kernel", "kl": "mha_kl_kernel",
                            "bwd": "mha_bwd (delta, dq and dkdv kernels, one call)"}[args.which]}
+        if dev["peak_tflops_from_device"]:
+            roof["peak_from_device"] = dev["peak_tflops_from_device"]
+            roof["frac_of_device_peak"] = round(achieved / dev["peak_tflops_from_device"], 4)
+        if io_bytes:
+            # algorithmic bytes (Q, K, V read once, O and LSE written once) per second
+            roof["algorithmic_bytes"] = io_bytes
+            roof["achieved_gbs"] = round(io_bytes / (per.mean() * 1e-3) / 1e9, 1)
+            roof["achieved_gbs_frac"] = round(roof["achieved_gbs"] / PEAK_GBS, 4)
+            if traffic:
+                roof["traffic_gbs"] = round(traffic / (per.mean() * 1e-3) / 1e9, 1)
+        roof.update(sq_counters(w.name, args.which))
     roof["launch_ms"] = {"mean": round(float(per.mean()), 5),
                          "median": round(float(np.median(per)), 5),
-                         "min": round(float(per.min()), 5)}
+                         "min": round(float(per.min()), 5),
+                         "amortised_back_to_back": round(amortised_ms, 5)}
+    if flushed_ms is not None:
+        roof["mall_flushed"] = {"flush_mib": MALL_FLUSH_MIB, "launch_ms_median": round(flushed_ms, 5),
+                                "tflops": round(flops / (flushed_ms * 1e-3) / 1e12, 2),
+                                "achieved_gbs": round(w.io_bytes / (flushed_ms * 1e-3) / 1e9, 1)}
     line.update({
         "n_gpus": 1,
         "steps": K,
@@ -526,13 +679,17 @@ def main() -> int:
         "roofline": roof,
         "timed_wall_s": round(wall, 3),
         "kernel_source_sha256_16": kernel_source_hash(srcs[args.which]),
-        "device": torch.cuda.get_device_name(0),
+        "device": dev,
     })
     if not args.no_cpu_baseline:
         print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
               flush=True)
         if args.which == "fwd":
-            line["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
+            sys.path.insert(0, os.path.join(ROOT, "tests"))
+            step()  # one more launch: the outputs the parity line compares
+            torch.cuda.synchronize()
+            got = (o.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy())
+            line["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds, gpu=got)
         elif args.which == "bwd":
             line["cpu_baseline"] = cpu_baseline_bwd(w, qb, kb, vb, gb, args.cpu_seconds)
         elif args.which == "kl":

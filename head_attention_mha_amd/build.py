@@ -18,7 +18,7 @@ SOURCES = [os.path.join(CSRC, f) for f in
            ("mha_api.hip", "mha_fwd.hip", "mha_splitkv.hip", "mha_bwd.hip", "mha_kl.hip",
             "mha_proj.hip")]
 DEPS = [os.path.join(CSRC, f) for f in
-        ("mha_common.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp", "mha_split_kernel.hpp",
+        ("mha_common.hpp", "mha_validate.hpp", "mha_tiles.hpp", "mha_sync.hpp", "mha_fwd_kernel.hpp", "mha_split_kernel.hpp",
          "mha_bwd_kernel.hpp", "mha_kl_kernel.hpp", "mha_proj_kernel.hpp")]
 DEPS.append(os.path.join(ROOT, "include", "mha.h"))
 

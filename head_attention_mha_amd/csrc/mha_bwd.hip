@@ -1,65 +1,12 @@
-// C ABI of the attention backward: validation, template dispatch and launch
-// of the D, dQ and dK/dV kernels (contract in include/mha.h).
+// C ABI of the attention backward: template dispatch and launch of the D, dQ
+// and dK/dV kernels (contract in include/mha.h; argument checks in
+// mha_validate.hpp).
 #include "mha_bwd_kernel.hpp"
 #include "mha_common.hpp"
 
 using namespace mha_host;
 
 namespace {
-
-// Host-side checks of an mha_bwd call. `*empty_q`: no query rows (dQ and D
-// have no elements); `*empty_k`: no key rows (dK and dV have no elements).
-mha_status_t validate_bwd(const void* q, const void* k, const void* v, const void* o,
-                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                          float* delta, int B, int H, int Nq, int Nk, int d, int causal,
-                          float scale, int dtype, bool* empty_q, bool* empty_k) {
-  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return MHA_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return MHA_ERR_INVALID_ARG;
-  if (dtype != MHA_DTYPE_FP16 && dtype != MHA_DTYPE_BF16) return MHA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return MHA_ERR_INVALID_ARG;
-  if (d <= 0) return MHA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return MHA_ERR_UNSUPPORTED;
-
-  const size_t es = 2;
-  const size_t nq = (size_t)B * Nq * H * d;
-  const size_t nk = (size_t)B * Nk * H * d;
-  const size_t nl = (size_t)B * H * Nq;
-  *empty_q = (nl == 0);
-  *empty_k = (nk == 0);
-  if (*empty_q && *empty_k) return MHA_OK;
-  if (!*empty_q && Nk < 1) return MHA_ERR_INVALID_ARG;  // softmax over no keys
-
-  if (!*empty_q) {
-    if (!q || !o || !dout || !lse || !dq || !delta) return MHA_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
-        !aligned(lse, 4) || !aligned(delta, 4))
-      return MHA_ERR_INVALID_ARG;
-  }
-  if (!*empty_k) {
-    if (!k || !v || !dk || !dv) return MHA_ERR_INVALID_ARG;
-    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16))
-      return MHA_ERR_INVALID_ARG;
-  }
-  // grid sizes of the three kernels must fit 31 bits
-  const long long nqb = ((long long)Nq + mha::bwd::kBQ - 1) / mha::bwd::kBQ;
-  const long long nkb = ((long long)Nk + mha::bwd::kBKV - 1) / mha::bwd::kBKV;
-  if ((long long)B * H * nqb > 0x7fffffffLL || (long long)B * H * nkb > 0x7fffffffLL ||
-      (long long)nl > 0x7fffffffLL)
-    return MHA_ERR_INVALID_ARG;
-
-  // every output is disjoint from every other buffer
-  const void* in[6] = {q, k, v, o, dout, lse};
-  const size_t in_n[6] = {nq * es, nk * es, nk * es, nq * es, nq * es, nl * 4};
-  void* out[4] = {dq, dk, dv, delta};
-  const size_t out_n[4] = {nq * es, nk * es, nk * es, nl * 4};
-  for (int a = 0; a < 4; ++a) {
-    for (int b = 0; b < 6; ++b)
-      if (overlap(out[a], out_n[a], in[b], in_n[b])) return MHA_ERR_INVALID_ARG;
-    for (int b = a + 1; b < 4; ++b)
-      if (overlap(out[a], out_n[a], out[b], out_n[b])) return MHA_ERR_INVALID_ARG;
-  }
-  return MHA_OK;
-}
 
 template <typename T, int D, bool C>
 mha_status_t launch_bwd(const mha::BwdParams& pd, const mha::BwdParams& pq,

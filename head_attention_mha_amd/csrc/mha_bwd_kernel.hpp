@@ -55,12 +55,9 @@ struct BwdParams {
 
 namespace bwd {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBQ = 32 * kWaves;   // query rows per dq workgroup
-constexpr int kBKV = 32 * kWaves;  // keys per dkdv workgroup
-constexpr int kBK = 64;            // keys per tile streamed by dq
-constexpr int kBQt = 32;           // queries per tile streamed by dkdv
+// kWaves, kThreads, kBQ (query rows per dq workgroup), kBKV (keys per dkdv
+// workgroup), kBK (keys per dq tile) and kBQt (queries per dkdv tile) are in
+// mha_tiles.hpp
 constexpr float kLog2e = 1.4426950408889634f;
 
 using mha::lds_read_tr16;

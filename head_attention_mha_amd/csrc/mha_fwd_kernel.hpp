@@ -70,6 +70,8 @@
 
 #include <type_traits>
 
+#include "mha_tiles.hpp"
+
 namespace mha {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -138,10 +140,9 @@ struct Params {
   int n_blocks;      // B * H * n_qtiles
 };
 
-constexpr int kWaves = 8;          // two groups of four: one wave of each per SIMD
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBQ = 32 * kWaves;  // query rows per workgroup (32 per wave)
-constexpr int kBK = 64;           // keys per tile
+// kWaves (two groups of four: one wave of each per SIMD), kThreads, kBQ
+// (query rows per workgroup, 32 per wave) and kBK (keys per tile) are in
+// mha_tiles.hpp.
 // The O rescale is deferred while a row's running max stays within 2^8 (in
 // the exp2 domain) of the reference max the accumulators were scaled to.
 constexpr float kDeferLog2 = 8.0f;

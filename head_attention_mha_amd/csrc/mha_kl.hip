@@ -1,46 +1,12 @@
-// C ABI of the fused attention KL divergence: validation, template dispatch
-// and launch of mha_kl_kernel (contract in include/mha.h).
+// C ABI of the fused attention KL divergence: template dispatch and launch
+// of mha_kl_kernel (contract in include/mha.h; argument checks in
+// mha_validate.hpp).
 #include "mha_common.hpp"
 #include "mha_kl_kernel.hpp"
 
 using namespace mha_host;
 
 namespace {
-
-// Host-side checks of an mha_kl_fwd call; `*empty`: no query rows.
-mha_status_t validate_kl(const void* q1, const void* k1, const void* q2, const void* k2,
-                         float* kl, float* lse1, float* lse2, int B, int H, int Nq, int Nk,
-                         int d, int causal, float scale, int dtype, bool* empty) {
-  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return MHA_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return MHA_ERR_INVALID_ARG;
-  if (dtype != MHA_DTYPE_FP16 && dtype != MHA_DTYPE_BF16) return MHA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return MHA_ERR_INVALID_ARG;
-  if (d <= 0) return MHA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return MHA_ERR_UNSUPPORTED;
-  const size_t es = 2;
-  const size_t nq = (size_t)B * Nq * H * d;
-  const size_t nk = (size_t)B * Nk * H * d;
-  const size_t nl = (size_t)B * H * Nq;
-  *empty = (nl == 0);
-  if (*empty) return MHA_OK;
-  if (Nk < 1) return MHA_ERR_INVALID_ARG;  // a softmax over no keys is undefined
-  if (!q1 || !k1 || !q2 || !k2 || !kl || !lse1 || !lse2) return MHA_ERR_INVALID_ARG;
-  if (!aligned(q1, 16) || !aligned(k1, 16) || !aligned(q2, 16) || !aligned(k2, 16) ||
-      !aligned(kl, 4) || !aligned(lse1, 4) || !aligned(lse2, 4))
-    return MHA_ERR_INVALID_ARG;
-  const long long n_qtiles = ((long long)Nq + mha::kl::kBQ - 1) / mha::kl::kBQ;
-  if ((long long)B * H * n_qtiles > 0x7fffffffLL) return MHA_ERR_INVALID_ARG;
-  const void* in[4] = {q1, k1, q2, k2};
-  const size_t in_n[4] = {nq * es, nk * es, nq * es, nk * es};
-  float* out[3] = {kl, lse1, lse2};
-  for (int a = 0; a < 3; ++a) {
-    for (int b = 0; b < 4; ++b)
-      if (overlap(out[a], nl * 4, in[b], in_n[b])) return MHA_ERR_INVALID_ARG;
-    for (int b = a + 1; b < 3; ++b)
-      if (overlap(out[a], nl * 4, out[b], nl * 4)) return MHA_ERR_INVALID_ARG;
-  }
-  return MHA_OK;
-}
 
 template <typename T, int D, bool C>
 mha_status_t launch_kl(const mha::KlParams& p, hipStream_t stream) {

@@ -44,10 +44,8 @@ struct KlParams {
 };
 
 namespace kl {
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBQ = 32 * kWaves;  // query rows per workgroup
-constexpr int kBK = 64;           // keys per tile
+// kWaves, kThreads, kBQ (query rows per workgroup) and kBK (keys per tile)
+// are in mha_tiles.hpp
 constexpr float kLn2 = 0.69314718055994531f;
 }  // namespace kl
 

@@ -33,11 +33,8 @@ struct ProjParams {
 };
 
 namespace proj {
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 256;  // output features per workgroup
-constexpr int kBM = 256;  // tokens per workgroup
-constexpr int kBK = 64;   // K per stage
+// kWaves, kThreads, kBN (output features per workgroup), kBM (tokens per
+// workgroup) and kBK (K per stage) are in mha_tiles.hpp
 
 // 16-byte-chunk swizzle of the 128-byte stage rows: 8 consecutive rows, and
 // the 8 rows of each parity among 16 consecutive rows, use 8 different

@@ -45,9 +45,7 @@ struct SplitParams {
 
 namespace split {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxNq = 8;
+// kWaves, kThreads and kMaxNq are in mha_tiles.hpp
 constexpr float kLn2 = 0.69314718055994531f;
 
 // x summed over the 2^LOG lanes of its group (groups of 8 or 16 lanes), in

@@ -1,5 +1,6 @@
-// C ABI of the split-over-keys forward: validation, template dispatch and
-// launch of the partial and merge kernels (contract in include/mha.h).
+// C ABI of the split-over-keys forward: template dispatch and launch of the
+// partial and merge kernels (contract in include/mha.h; argument checks in
+// mha_validate.hpp).
 #include "mha_common.hpp"
 #include "mha_split_kernel.hpp"
 
@@ -7,45 +8,12 @@ using namespace mha_host;
 
 namespace {
 
-constexpr int kMaxSplits = 256;
-static_assert(kMaxSplits <= mha::split::kThreads, "the merge reads one LSE per thread");
-// Keys per split are a multiple of this (the partial kernel's block at d = 64).
-constexpr int kSplitAlign = 256;
+using mha::split::kMaxSplits;
+using mha::split::kSplitAlign;  // keys per split: a multiple of the partial kernel's block at d = 64
 
 int split_len(int Nk, int n_splits) {
   const long long per = ((long long)Nk + n_splits - 1) / n_splits;
   return (int)(((per + kSplitAlign - 1) / kSplitAlign) * kSplitAlign);
-}
-
-// Host-side checks of an mha_fwd_splitkv call.
-mha_status_t validate_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                              int B, int H, int Nq, int Nk, int d, int causal, float scale,
-                              int n_splits, float* o_part, float* lse_part, int dtype,
-                              bool* empty) {
-  bool e = false;
-  mha_status_t st = validate_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, 1, &e);
-  if (st != MHA_OK) return st;
-  if (n_splits < 1 || n_splits > kMaxSplits) return MHA_ERR_INVALID_ARG;
-  *empty = e;
-  if (e) return MHA_OK;
-  if (Nq > mha::split::kMaxNq) return MHA_ERR_UNSUPPORTED;
-  if ((long long)B * H * n_splits > 0x7fffffffLL || (long long)B * H * Nq > 0x7fffffffLL ||
-      (long long)Nk + kSplitAlign > 0x7fffffffLL)
-    return MHA_ERR_INVALID_ARG;
-  if (!o_part || !lse_part || !aligned(o_part, 16) || !aligned(lse_part, 4))
-    return MHA_ERR_INVALID_ARG;
-  const size_t es = 2;
-  const size_t nq = (size_t)B * Nq * H * d;
-  const size_t nk = (size_t)B * Nk * H * d;
-  const size_t nl = (size_t)B * H * Nq;
-  const size_t n_op = (size_t)n_splits * nl * d * 4, n_lp = (size_t)n_splits * nl * 4;
-  const void* bufs[5] = {q, k, v, o, lse};
-  const size_t sizes[5] = {nq * es, nk * es, nk * es, nq * es, nl * 4};
-  for (int i = 0; i < 5; ++i)
-    if (overlap(o_part, n_op, bufs[i], sizes[i]) || overlap(lse_part, n_lp, bufs[i], sizes[i]))
-      return MHA_ERR_INVALID_ARG;
-  if (overlap(o_part, n_op, lse_part, n_lp)) return MHA_ERR_INVALID_ARG;
-  return MHA_OK;
 }
 
 template <typename T, int D, int NQ, bool C>

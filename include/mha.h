@@ -63,7 +63,12 @@ typedef enum { MHA_DTYPE_FP16 = 0, MHA_DTYPE_BF16 = 1 } mha_dtype_t;
  *          B*H*Nq > 0 (a softmax over no keys is undefined)
  *   d      head dimension: 64 or 128
  *   causal 0 or 1 (1: key j visible to query i iff j <= i)
- *   scale  softmax scale applied to q.k, finite and > 0 (typically 1/sqrt(d))
+ *   scale  softmax scale applied to q.k, finite and > 0 (typically 1/sqrt(d)).
+ *          The definition itself admits any finite scale; the restriction
+ *          to scale > 0 is this implementation's: the kernels defer the
+ *          rescale of O while a row's running maximum of the raw scores q.k
+ *          grows by less than a fixed margin, which assumes exp(scale * x)
+ *          increases with x.
  *   stream hipStream_t to enqueue on, passed as void*; NULL = default stream
  *   dtype  MHA_DTYPE_FP16 or MHA_DTYPE_BF16
  *
@@ -81,7 +86,11 @@ typedef enum { MHA_DTYPE_FP16 = 0, MHA_DTYPE_BF16 = 1 } mha_dtype_t;
  * MHA_ERR_INVALID_ARG and write nothing): q, k, v, o non-null and 16-byte
  * aligned, lse non-null and 4-byte aligned (null is accepted only for a
  * tensor with zero elements); o and lse must not overlap each other or any
- * input. An empty problem (B*H*Nq == 0) returns MHA_OK and enqueues nothing.
+ * input; H*d <= 2^23 (a workgroup addresses 256 token rows with 32-bit byte
+ * offsets); fewer than 2^31 workgroups (B*H*ceil(Nq/256)); no tensor above
+ * 2^60 elements. Sizes are multiplied with overflow checks, so any int
+ * arguments are safe to pass. An empty problem (B*H*Nq == 0) returns MHA_OK
+ * and enqueues nothing.
  *
  * Errors are reported only through the return value: nothing is printed,
  * nothing aborts, no C++ exception crosses this boundary. A fault inside the
@@ -183,7 +192,9 @@ MHA_API mha_status_t mha_kl_fwd(const void* q1, const void* k1, const void* q2,
  *   bias   device pointer, [E], `dtype`, 8-byte aligned; or NULL for none
  *   y      device pointer, [B, Nq, E], `dtype` (written; fp32 accumulation
  *          rounded to nearest even), 16-byte aligned
- *   B, Nq, H, d, E  sizes, >= 0; H*d must be a multiple of 64 and E of 4
+ *   B, Nq, H, d, E  sizes, >= 0; H*d at most 2^23 (32-bit offsets within
+ *                   a 256-row tile) and B*Nq below 2^31 (else
+ *                   MHA_ERR_INVALID_ARG); H*d a multiple of 64 and E of 4
  *                   (else MHA_ERR_UNSUPPORTED)
  *   stream, dtype   as for mha_fwd
  *

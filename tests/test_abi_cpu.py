@@ -314,3 +314,46 @@ def test_proj_empty_and_no_bias(lib):
     import torch
     if not torch.cuda.is_available():
         assert call_proj(bias=None) == mha.MHA_ERR_DEVICE  # a null bias is valid
+
+
+# -------------------------------------- 32-bit offsets within a tile of rows
+# A workgroup addresses up to 256 token rows of H*d elements (or 256 rows of
+# K = H*d for the projection) through 32-bit byte offsets, so a row may hold
+# at most 2^23 elements; every entry point rejects more before any HIP call.
+@pytest.mark.parametrize("entry", ["fwd", "bwd", "kl", "split", "proj"])
+def test_rows_past_2p23_elements_are_rejected(lib, entry):
+    big = dict(H=65537, d=128, Nq=1, Nk=1)
+    if entry == "fwd":
+        st = call(**big)
+    elif entry == "bwd":
+        st = call_bwd(**big)
+    elif entry == "kl":
+        st = call_kl(**big)
+    elif entry == "split":
+        st = call_split(**big, n_splits=1)
+    else:
+        st = call_proj(H=65537, d=128, Nq=1, B=1)
+    assert st == mha.MHA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("entry", ["fwd", "bwd", "kl", "proj"])
+def test_rows_of_2p23_elements_pass_validation(lib, entry):
+    # passing every host check, the call reaches the device query; only run
+    # where there is no device (the buffers here are not real)
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    at = dict(H=65536, d=128, Nq=1, Nk=1)
+    st = {"fwd": lambda: call(**at), "bwd": lambda: call_bwd(**at),
+          "kl": lambda: call_kl(**at),
+          "proj": lambda: call_proj(H=65536, d=128, Nq=1, B=1, E=4)}[entry]()
+    assert st == mha.MHA_ERR_DEVICE
+
+
+def test_huge_sizes_are_rejected_without_overflow(lib):
+    imax = 2**31 - 1
+    assert call(B=imax, H=1, Nq=imax, Nk=imax) == mha.MHA_ERR_INVALID_ARG
+    assert call(B=imax, H=65536, Nq=imax, Nk=imax, d=128) == mha.MHA_ERR_INVALID_ARG
+    assert call_bwd(B=imax, H=2, Nq=imax, Nk=imax) == mha.MHA_ERR_INVALID_ARG
+    assert call_kl(B=imax, H=4, Nq=imax, Nk=1) == mha.MHA_ERR_INVALID_ARG
+    assert call_proj(B=imax, Nq=imax, H=imax, d=imax, E=imax) == mha.MHA_ERR_INVALID_ARG

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from parity import assert_parity, compare
+from parity import assert_parity, compare, report
 
 pytestmark = pytest.mark.gpu
 
@@ -82,7 +82,7 @@ def check(torch, mha, qb, kb, vb, dtype, causal, scale, n_splits, label, ws=None
     O_ref, L_ref = oracle.attention_fwd(*(wl.bits_to_f64(x, dtype) for x in (qb, kb, vb)),
                                         causal, scale)
     st = compare(o_bits, lse, O_ref, L_ref, dtype)
-    sys.__stderr__.write(f"[splitkv-parity] {label}: {st}\n")
+    sys.__stderr__.write(f"[splitkv-parity] {report(st, label)}\n")
     assert_parity(st, label)
     return st
 

@@ -5,6 +5,7 @@ import pytest
 
 import oracle
 import workloads as wl
+from parity import rounding_floor
 
 
 def test_bf16_round_to_nearest_even():
@@ -64,28 +65,35 @@ def test_workload_table():
     assert w.scale == float(np.float32(1 / np.sqrt(128)))
 
 
-def _floor_rows(w, rng):
-    head = np.arange(min(w.Nq, 64))
-    rest = rng.choice(w.Nq, size=min(w.Nq, 64), replace=False)
-    return np.unique(np.concatenate([head, rest]))
+# The largest rounding floor |nearest output value - exact O| of each
+# workload, over every element (b, row, h, c), from the fp64 oracle: only
+# decoder_causal has an element the output format cannot bring within the
+# 1e-2 max-abs bar, at row 1 (an average of two values) where |O| > 4.
+FLOOR_OVER_BAR = {"decoder_causal": ((2, 1, 11, 72), 0.0138105)}
 
 
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))
 def test_output_rounding_floor(name):
-    """The parity bound on O is max-abs <= 1e-2 against the unrounded fp64 O.
-    Rounding the exact O to the output dtype already costs half an ulp; check
-    on the rows where |O| is largest (the first causal rows) plus a random
-    sample that this unavoidable floor stays well inside the bound."""
+    """The parity bar on O is a flat max-abs <= 1e-2 against the unrounded
+    fp64 O. Rounding the exact O to the output type already costs up to half
+    an ulp; compute that unavoidable floor over every element of the workload
+    and state where it exceeds the bar (exactly one element, in the masked
+    decoder workload) and that it stays below 8e-3 everywhere else."""
     w = wl.WORKLOADS[name]
     q, k, v = (wl.bits_to_f64(x, w.dtype) for x in wl.make_inputs(w))
-    rows = _floor_rows(w, np.random.default_rng(0))
-    heads = range(w.H) if w.H * w.B <= 16 else range(0, w.H, max(1, w.H // 4))
-    worst = 0.0
-    for b in range(min(w.B, 2)):
-        for h in heads:
-            O, _ = oracle.attention_fwd(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1],
-                                        v[b:b + 1, :, h:h + 1], w.causal, w.scale, rows=rows)
-            Or = wl.bits_to_f64(wl.round_bits(O.astype(np.float32), w.dtype), w.dtype)
-            worst = max(worst, float(np.abs(Or - O).max()))
-    print(f"{name}: output rounding floor on sampled rows = {worst:.3e}")
-    assert worst < 8e-3
+    worst, at, n_over = -1.0, None, 0
+    for r0 in range(0, w.Nq, 2048):
+        rows = np.arange(r0, min(w.Nq, r0 + 2048))
+        O, _ = oracle.attention_fwd(q, k, v, w.causal, w.scale, rows=rows)
+        f = rounding_floor(O, w.dtype)
+        n_over += int((f > 1e-2).sum())
+        i = np.unravel_index(int(np.argmax(f)), f.shape)
+        if f[i] > worst:
+            worst, at = float(f[i]), (int(i[0]), int(rows[i[1]]), int(i[2]), int(i[3]))
+    print(f"{name}: output rounding floor {worst:.4e} at (b, row, h, c) = {at}; "
+          f"{n_over} element(s) above 1e-2")
+    if name in FLOOR_OVER_BAR:
+        want_at, want = FLOOR_OVER_BAR[name]
+        assert at == want_at and worst == pytest.approx(want, abs=1e-6) and n_over == 1
+    else:
+        assert worst < 8e-3 and n_over == 0
