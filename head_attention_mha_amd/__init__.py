@@ -12,13 +12,16 @@ from ._binding import (  # noqa: F401
     MHA_ERR_DEVICE,
     MHA_ERR_INVALID_ARG,
     MHA_ERR_LAUNCH,
+    MHA_ERR_SCRATCH_TOO_SMALL,
     MHA_ERR_UNSUPPORTED,
+    MHA_NOALLOC_SCRATCH_BYTES,
     MHA_OK,
     MhaError,
     attention,
     attention_backward,
     attention_kl,
     attention_splitkv,
+    attention_splitkv_noalloc,
     load_library,
     out_proj,
     mha_abi_version,
@@ -26,6 +29,7 @@ from ._binding import (  # noqa: F401
     mha_kl_fwd,
     mha_out_proj,
     mha_fwd_splitkv,
+    mha_fwd_splitkv_noalloc,
     mha_fwd_splitkv_splits,
     mha_fwd,
     mha_status_string,

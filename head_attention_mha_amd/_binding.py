@@ -22,11 +22,14 @@ MHA_ERR_INVALID_ARG = 1
 MHA_ERR_UNSUPPORTED = 2
 MHA_ERR_DEVICE = 3
 MHA_ERR_LAUNCH = 4
+MHA_ERR_SCRATCH_TOO_SMALL = 5
+MHA_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/mha.h
 MHA_DTYPE_FP16 = 0
 MHA_DTYPE_BF16 = 1
 
 # Every symbol include/mha.h declares.
-EXPORTED_SYMBOLS = ("mha_fwd", "mha_fwd_splitkv", "mha_fwd_splitkv_splits", "mha_bwd",
+EXPORTED_SYMBOLS = ("mha_fwd", "mha_fwd_splitkv", "mha_fwd_splitkv_noalloc",
+                    "mha_fwd_splitkv_splits", "mha_bwd",
                     "mha_kl_fwd", "mha_out_proj", "mha_status_string", "mha_abi_version")
 
 _lib = None
@@ -60,6 +63,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int,
+    ]
+    lib.mha_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.mha_fwd_splitkv_noalloc.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
     ]
     lib.mha_fwd_splitkv_splits.restype = ctypes.c_int
     lib.mha_fwd_splitkv_splits.argtypes = [ctypes.c_int] * 4
@@ -113,6 +122,15 @@ def mha_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq
                                               stream, int(dtype)))
 
 
+def mha_fwd_splitkv_noalloc(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Nq: int,
+                            Nk: int, d: int, causal: int, scale: float, n_splits: int,
+                            stream: int | None, dtype: int) -> int:
+    """Call the C entry point with raw pointers; returns the status code."""
+    return int(load_library().mha_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d,
+                                                      int(causal), float(scale), int(n_splits),
+                                                      stream, int(dtype)))
+
+
 def mha_fwd_splitkv_splits(B: int, H: int, Nq: int, Nk: int) -> int:
     return int(load_library().mha_fwd_splitkv_splits(B, H, Nq, Nk))
 
@@ -145,6 +163,38 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
                              n_splits, o_part.data_ptr(), lse_part.data_ptr(), stream, dt)
     if st != MHA_OK:
         raise MhaError(st, "mha_fwd_splitkv")
+    return out, lse
+
+
+def attention_splitkv_noalloc(q, k, v, out, lse, causal: bool = False,
+                              scale: float | None = None, n_splits: int | None = None,
+                              stream=None):
+    """``attention_splitkv`` into the caller's ``out`` [B, Nq, H, d] and
+    ``lse`` [B, H, Nq] fp32, using the library's fixed per-GPU scratch for the
+    partial results: nothing is allocated, so the call can sit in code that
+    must not allocate (e.g. under graph capture). Raises MhaError with
+    MHA_ERR_SCRATCH_TOO_SMALL when the problem's workspace exceeds
+    MHA_NOALLOC_SCRATCH_BYTES."""
+    import torch
+
+    B, Nq, H, d, Nk = _check_qkv(q, k, v)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = mha_fwd_splitkv_splits(B, H, Nq, Nk)
+    dt = MHA_DTYPE_BF16 if q.dtype == torch.bfloat16 else MHA_DTYPE_FP16
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = mha_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, H, Nq, Nk, d, int(bool(causal)),
+                                     float(scale), n_splits, stream, dt)
+    if st != MHA_OK:
+        raise MhaError(st, "mha_fwd_splitkv_noalloc")
     return out, lse
 
 

@@ -52,6 +52,9 @@ const char* mha_status_string(int status) {
       return "no usable HIP device";
     case MHA_ERR_LAUNCH:
       return "kernel launch failed";
+    case MHA_ERR_SCRATCH_TOO_SMALL:
+      return "the problem's split workspace exceeds the fixed scratch of mha_fwd_splitkv_noalloc "
+             "(MHA_NOALLOC_SCRATCH_BYTES); use mha_fwd_splitkv with a workspace";
     default:
       return "unknown status";
   }

@@ -1,12 +1,50 @@
-// C ABI of the split-over-keys forward: template dispatch and launch of the
-// partial and merge kernels (contract in include/mha.h; argument checks in
+// C ABI of the split-over-keys forward, with a caller workspace or with the
+// library's fixed scratch array: template dispatch and launch of the partial
+// and merge kernels (contract in include/mha.h; argument checks in
 // mha_validate.hpp).
 #include "mha_common.hpp"
 #include "mha_split_kernel.hpp"
 
+#include <atomic>
+#include <mutex>
+
 using namespace mha_host;
 
 namespace {
+
+// Workspace of mha_fwd_splitkv_noalloc: one fixed array per GPU in device
+// memory, held until the process ends. In host code its name is only a
+// host-side stand-in; host code uses the device address that
+// hipGetSymbolAddress returns for it, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[MHA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array.
+mha_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return MHA_ERR_DEVICE;
+  }
+  if (dev >= kMaxScratchDevices) return MHA_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+        (void)hipGetLastError();
+        return MHA_ERR_DEVICE;
+      }
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MHA_OK;
+}
 
 using mha::split::kMaxSplits;
 using mha::split::kSplitAlign;  // keys per split: a multiple of the partial kernel's block at d = 64
@@ -48,6 +86,33 @@ mha_status_t dispatch_split(const mha::SplitParams& p, int d, bool causal, hipSt
   return causal ? dispatch_split_nq<T, 128, true>(p, s) : dispatch_split_nq<T, 128, false>(p, s);
 }
 
+// Launch of the partial and merge kernels for a validated call whose
+// workspace is (o_part, lse_part).
+mha_status_t run_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int Nq, int Nk, int d, int causal, float scale, int n_splits,
+                       float* o_part, float* lse_part, void* stream, int dtype) {
+  mha::SplitParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.n_splits = n_splits;
+  p.split_len = split_len(Nk, n_splits);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MHA_DTYPE_BF16) return dispatch_split<mha::BF16>(p, d, causal != 0, s);
+  return dispatch_split<mha::F16>(p, d, causal != 0, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,27 +138,28 @@ mha_status_t mha_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   if (st != MHA_OK || empty) return st;
   st = check_device();
   if (st != MHA_OK) return st;
+  return run_split(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, n_splits, o_part, lse_part,
+                   stream, dtype);
+}
 
-  mha::SplitParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<uint16_t*>(o);
-  p.lse = lse;
-  p.o_part = o_part;
-  p.lse_part = lse_part;
-  p.B = B;
-  p.H = H;
-  p.Nq = Nq;
-  p.Nk = Nk;
-  p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.n_splits = n_splits;
-  p.split_len = split_len(Nk, n_splits);
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == MHA_DTYPE_BF16) return dispatch_split<mha::BF16>(p, d, causal != 0, s);
-  return dispatch_split<mha::F16>(p, d, causal != 0, s);
+mha_status_t mha_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int B, int H, int Nq, int Nk, int d, int causal,
+                                     float scale, int n_splits, void* stream, int dtype) {
+  bool empty = false;
+  mha_status_t st = validate_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale,
+                                             n_splits, dtype, MHA_NOALLOC_SCRATCH_BYTES, &empty);
+  if (st != MHA_OK || empty) return st;
+  st = check_device();
+  if (st != MHA_OK) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != MHA_OK) return st;
+  // partial outputs first, the partial LSEs after them (256-byte aligned)
+  float* o_part = static_cast<float*>(ws);
+  float* lse_part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
+                                             splitkv_opart_bytes(B, H, Nq, d, n_splits));
+  return run_split(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, n_splits, o_part, lse_part,
+                   stream, dtype);
 }
 
 }  // extern "C"

@@ -98,11 +98,11 @@ inline mha_status_t validate_fwd(const void* q, const void* k, const void* v, vo
   return MHA_OK;
 }
 
-// Host-side checks of an mha_fwd_splitkv call.
-inline mha_status_t validate_splitkv(const void* q, const void* k, const void* v, void* o,
-                                     float* lse, int B, int H, int Nq, int Nk, int d, int causal, float scale,
-                              int n_splits, float* o_part, float* lse_part, int dtype,
-                              bool* empty) {
+// Host-side checks of an mha_fwd_splitkv call, apart from its workspace.
+inline mha_status_t validate_splitkv_args(const void* q, const void* k, const void* v, void* o,
+                                          float* lse, int B, int H, int Nq, int Nk, int d,
+                                          int causal, float scale, int n_splits, int dtype,
+                                          bool* empty) {
   bool e = false;
   mha_status_t st = validate_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, 1, &e);
   if (st != MHA_OK) return st;
@@ -115,20 +115,57 @@ inline mha_status_t validate_splitkv(const void* q, const void* k, const void* v
       (long long)Nk + mha::split::kSplitAlign > kMaxGrid)
     return MHA_ERR_INVALID_ARG;
   if (!product(&n_opl, {n_splits, B, H, Nq, d}, kMaxElems)) return MHA_ERR_INVALID_ARG;
+  return MHA_OK;
+}
+
+// Bytes of the split-KV workspace: the partial outputs [n_splits, B, H, Nq, d]
+// fp32, padded to 256 bytes, then the partial LSEs [n_splits, B, H, Nq] fp32.
+// Valid for sizes validate_splitkv_args accepted.
+inline size_t splitkv_opart_bytes(int B, int H, int Nq, int d, int n_splits) {
+  const size_t n = (size_t)n_splits * B * H * Nq * d * 4;
+  return (n + 255) / 256 * 256;
+}
+inline size_t splitkv_workspace_bytes(int B, int H, int Nq, int d, int n_splits) {
+  return splitkv_opart_bytes(B, H, Nq, d, n_splits) + (size_t)n_splits * B * H * Nq * 4;
+}
+
+// Host-side checks of an mha_fwd_splitkv call with a caller workspace.
+inline mha_status_t validate_splitkv(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int B, int H, int Nq, int Nk, int d, int causal,
+                                     float scale, int n_splits, float* o_part, float* lse_part,
+                                     int dtype, bool* empty) {
+  mha_status_t st = validate_splitkv_args(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale,
+                                          n_splits, dtype, empty);
+  if (st != MHA_OK || *empty) return st;
   if (!o_part || !lse_part || !aligned(o_part, 16) || !aligned(lse_part, 4))
     return MHA_ERR_INVALID_ARG;
-  // sizes below are bounded by the products checked here and in validate_fwd
+  // sizes below are bounded by the products validate_splitkv_args checked
   const size_t es = 2;
   const size_t nq = (size_t)B * Nq * H * d;
   const size_t nk = (size_t)B * Nk * H * d;
   const size_t nl = (size_t)B * H * Nq;
-  const size_t n_op = (size_t)n_opl * 4, n_lp = (size_t)n_splits * nl * 4;
+  const size_t n_op = (size_t)n_splits * nl * d * 4, n_lp = (size_t)n_splits * nl * 4;
   const void* bufs[5] = {q, k, v, o, lse};
   const size_t sizes[5] = {nq * es, nk * es, nk * es, nq * es, nl * 4};
   for (int i = 0; i < 5; ++i)
     if (overlap(o_part, n_op, bufs[i], sizes[i]) || overlap(lse_part, n_lp, bufs[i], sizes[i]))
       return MHA_ERR_INVALID_ARG;
   if (overlap(o_part, n_op, lse_part, n_lp)) return MHA_ERR_INVALID_ARG;
+  return MHA_OK;
+}
+
+// Host-side checks of an mha_fwd_splitkv_noalloc call: as mha_fwd_splitkv's,
+// and the workspace must fit the library's fixed scratch of `scratch_bytes`
+// (MHA_ERR_SCRATCH_TOO_SMALL otherwise).
+inline mha_status_t validate_splitkv_noalloc(const void* q, const void* k, const void* v,
+                                             void* o, float* lse, int B, int H, int Nq, int Nk,
+                                             int d, int causal, float scale, int n_splits,
+                                             int dtype, size_t scratch_bytes, bool* empty) {
+  mha_status_t st = validate_splitkv_args(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale,
+                                          n_splits, dtype, empty);
+  if (st != MHA_OK || *empty) return st;
+  if (splitkv_workspace_bytes(B, H, Nq, d, n_splits) > scratch_bytes)
+    return MHA_ERR_SCRATCH_TOO_SMALL;
   return MHA_OK;
 }
 

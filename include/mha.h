@@ -43,7 +43,9 @@ typedef enum {
   MHA_ERR_INVALID_ARG = 1, /* a null/misaligned/overlapping pointer, a bad size, flag or scale */
   MHA_ERR_UNSUPPORTED = 2, /* valid but not implemented: head dim other than 64/128, device not gfx950 */
   MHA_ERR_DEVICE = 3,      /* no usable HIP device (e.g. a host without a GPU) */
-  MHA_ERR_LAUNCH = 4       /* the kernel launch itself failed */
+  MHA_ERR_LAUNCH = 4,      /* the kernel launch itself failed */
+  MHA_ERR_SCRATCH_TOO_SMALL = 5 /* mha_fwd_splitkv_noalloc: the problem's workspace exceeds
+                                   MHA_NOALLOC_SCRATCH_BYTES */
 } mha_status_t;
 
 /* Element type of Q, K, V and O (LSE is always fp32). */
@@ -135,6 +137,38 @@ MHA_API mha_status_t mha_fwd_splitkv(const void* q, const void* k, const void* v
                                      float* lse, int B, int H, int Nq, int Nk, int d,
                                      int causal, float scale, int n_splits, float* o_part,
                                      float* lse_part, void* stream, int dtype);
+
+/*
+ * mha_fwd_splitkv_noalloc -- mha_fwd_splitkv without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory:
+ * code being captured into a HIP graph, tight serving loops, and harnesses
+ * that forbid hipMalloc during a step.
+ *
+ * The partial outputs and LSEs go to a scratch array the library holds in
+ * device memory: one per GPU, MHA_NOALLOC_SCRATCH_BYTES bytes, kept from the
+ * library's first use of that device until the process ends. The call
+ * allocates nothing (no hipMalloc/hipFree, no allocating
+ * library routine): its first call on a device only looks up the array's
+ * device address. The workspace a call needs,
+ *     n_splits*B*H*Nq*d*4 bytes (rounded up to 256) + n_splits*B*H*Nq*4 bytes,
+ * must fit: larger problems return MHA_ERR_SCRATCH_TOO_SMALL and enqueue
+ * nothing (use mha_fwd_splitkv with a workspace of their own). E.g. at the
+ * default n_splits, B=1, H=32, Nq=1, Nk=32768, d=128 needs 1.1 MB.
+ *
+ * Arguments, results and other errors: as for mha_fwd_splitkv, without
+ * o_part and lse_part. The kernels overwrite every workspace entry they
+ * read, so nothing carries over from the previous call.
+ *
+ * Concurrency: every call on one GPU uses that GPU's one scratch array.
+ * Calls that may run at the same time on one GPU (on different streams, or
+ * from different host threads onto different streams) race on it and give
+ * undefined results; calls on one stream run in order and are safe.
+ */
+#define MHA_NOALLOC_SCRATCH_BYTES (16u << 20)
+MHA_API mha_status_t mha_fwd_splitkv_noalloc(const void* q, const void* k, const void* v,
+                                             void* o, float* lse, int B, int H, int Nq, int Nk,
+                                             int d, int causal, float scale, int n_splits,
+                                             void* stream, int dtype);
 
 /*
  * Suggested n_splits for mha_fwd_splitkv: enough splits for about 2048

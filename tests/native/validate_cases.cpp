@@ -121,6 +121,24 @@ void split_cases() {
          validate_splitkv(buf(0), buf(1), buf(2), buf(3), fbuf(4), 1, 1, 1, 16, 64, 0, 0.1f, 2,
                           fbuf(1), fbuf(6), MHA_DTYPE_FP16, &e), MHA_ERR_INVALID_ARG);
   expect("split H*d > 2^23", sp(1, 65537, 1, 16, 128, 1), MHA_ERR_INVALID_ARG);
+
+  // the no-allocation variant: its workspace must fit the fixed scratch
+  auto na = [&](int B, int H, int Nq, int Nk, int d, int n, size_t cap) {
+    return validate_splitkv_noalloc(buf(0), buf(1), buf(2), buf(3), fbuf(4), B, H, Nq, Nk, d, 0,
+                                    0.1f, n, MHA_DTYPE_BF16, cap, &e);
+  };
+  const size_t cap = 16u << 20;
+  expect("noalloc decode fits", na(1, 32, 1, 32768, 128, 64, cap), MHA_OK);
+  // 63 splits x 512 rows x 129 floats fits in 16 MiB, 64 do not
+  expect("noalloc 63 splits fit", na(1, 64, 8, 256, 128, 63, cap), MHA_OK);
+  expect("noalloc 64 splits too large", na(1, 64, 8, 256, 128, 64, cap), MHA_ERR_SCRATCH_TOO_SMALL);
+  // exactly at the capacity: o_part 256 bytes (padded), lse_part 256 bytes
+  expect("noalloc exactly at capacity", na(1, 1, 1, 16, 64, 1, 256 + 4), MHA_OK);
+  expect("noalloc one byte short", na(1, 1, 1, 16, 64, 1, 256 + 3), MHA_ERR_SCRATCH_TOO_SMALL);
+  expect("noalloc checks the arguments first", na(1, 1, 9, 16, 64, 1, cap), MHA_ERR_UNSUPPORTED);
+  expect("noalloc bad splits", na(1, 1, 1, 16, 64, 0, cap), MHA_ERR_INVALID_ARG);
+  expect("noalloc empty", na(0, 1, 1, 16, 64, 4, 0), MHA_OK);
+  expect("noalloc huge", na(INT_MAX, INT_MAX, 8, INT_MAX, 128, 256, cap), MHA_ERR_INVALID_ARG);
 }
 
 void bwd_cases() {

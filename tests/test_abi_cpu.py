@@ -357,3 +357,39 @@ def test_huge_sizes_are_rejected_without_overflow(lib):
     assert call_bwd(B=imax, H=2, Nq=imax, Nk=imax) == mha.MHA_ERR_INVALID_ARG
     assert call_kl(B=imax, H=4, Nq=imax, Nk=1) == mha.MHA_ERR_INVALID_ARG
     assert call_proj(B=imax, Nq=imax, H=imax, d=imax, E=imax) == mha.MHA_ERR_INVALID_ARG
+
+
+# -------------------------------------------------- mha_fwd_splitkv_noalloc
+def call_noalloc(**kw):
+    a = dict(GOOD_SPLIT)
+    a.update(kw)
+    return mha.mha_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                       a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                                       a["n_splits"], a["stream"], a["dtype"])
+
+
+def test_noalloc_refuses_a_workspace_over_the_scratch(lib):
+    # 64 splits x 1*64*8 rows x (128 + 1) floats > 16 MiB (checked before any HIP call)
+    assert mha.MHA_NOALLOC_SCRATCH_BYTES == 16 << 20
+    st = call_noalloc(B=1, H=64, Nq=8, Nk=256, d=128, n_splits=64)
+    assert st == mha.MHA_ERR_SCRATCH_TOO_SMALL
+    assert "scratch" in mha.mha_status_string(st)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(n_splits=0), mha.MHA_ERR_INVALID_ARG),
+    (dict(n_splits=257), mha.MHA_ERR_INVALID_ARG),
+    (dict(Nq=9), mha.MHA_ERR_UNSUPPORTED),
+    (dict(H=65537, d=128, Nq=1, Nk=1, n_splits=1), mha.MHA_ERR_INVALID_ARG),
+], ids=lambda x: str(x))
+def test_noalloc_validation_rejects(lib, kw, want):
+    assert call_noalloc(**kw) == want
+
+
+def test_noalloc_no_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call_noalloc() == mha.MHA_ERR_DEVICE
+    assert call_noalloc(B=0) == mha.MHA_OK
