@@ -110,8 +110,12 @@ def sq_counters(workload: str, which: str = "fwd") -> dict:
     """MFMA busy fraction and the engine clock under load from the committed
     SQ/GRBM counter summary (None where it is missing or stale)."""
     f = profile_fields("sq_counters", workload, which)
-    return {"mfma_busy": _float(f, "mfma_busy_frac"),
-            "sclk_mhz_under_load": _float(f, "grbm_sclk_mhz")}
+    out = {"mfma_busy": _float(f, "mfma_busy_frac"),
+           "sclk_mhz_under_load": _float(f, "grbm_sclk_mhz")}
+    lb = _float(f, "mfma_busy_frac_lower_bound")
+    if lb is not None:  # dispatch too short for the engine-cycle count
+        out["mfma_busy_lower_bound"] = lb
+    return out
 
 
 def device_info(torch) -> dict:
@@ -655,6 +659,11 @@ def main() -> int:
             if traffic:
                 roof["traffic_gbs"] = round(traffic / (per.mean() * 1e-3) / 1e9, 1)
         roof.update(sq_counters(w.name, args.which))
+        if roof.get("sclk_mhz_under_load") and dev["cus"]:
+            # the dense ceiling at the engine clock the counters saw under this load
+            pk = dev["cus"] * roof["sclk_mhz_under_load"] * 1e6 * MFMA_FLOP_PER_CLK_PER_CU / 1e12
+            roof["peak_at_sclk_under_load"] = round(pk, 1)
+            roof["frac_at_sclk_under_load"] = round(achieved / pk, 4)
     roof["launch_ms"] = {"mean": round(float(per.mean()), 5),
                          "median": round(float(np.median(per)), 5),
                          "min": round(float(per.min()), 5),
