@@ -54,6 +54,7 @@ mha_status_t mha_kl_fwd(const void* q1, const void* k1, const void* q2, const vo
   p.Nk = Nk;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.defer_raw = mha::kDeferLog2 / p.scale_log2;
   p.n_tiles = (Nq + mha::kl::kBQ - 1) / mha::kl::kBQ;
   p.n_blocks = B * H * p.n_tiles;
 

@@ -4,9 +4,9 @@
 //
 // in one pass over the keys, without materialising either Nq x Nk matrix
 // ("StreamKL", Methodology section 1). Each row keeps five running scalars:
-// the maxima m1, m2 of the two score rows, the sums l1, l2 of exp(S_t - m_t)
-// and acc = sum_j exp(S1_ij - m1)(S1_ij - S2_ij), all rescaled when a
-// maximum grows; at the end KL = acc / l1 + LSE2 - LSE1 with
+// reference maxima m1, m2 of the two score rows, the sums l1, l2 of
+// exp(S_t - m_t) and acc = sum_j exp(S1_ij - m1)(S1_ij - S2_ij), all rescaled
+// when a maximum outgrows its reference by more than 2^8 (exp2 domain); at the end KL = acc / l1 + LSE2 - LSE1 with
 // LSE_t = m_t + log l_t. There is no P.V product: acc is one number per row,
 // not a row of an output matrix.
 //
@@ -39,6 +39,7 @@ struct KlParams {
   int B, H, Nq, Nk;
   float scale;       // softmax scale of both distributions (> 0)
   float scale_log2;  // scale * log2(e)
+  float defer_raw;   // rescale threshold in raw-score units: 8 / scale_log2
   int n_blocks;      // workgroups launched
   int n_tiles;       // query blocks per (b, h)
 };
@@ -150,13 +151,19 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
   }
 
   // running state of this lane's half of the row (m shared by both halves):
-  // maxima of the raw scores, sums in the exp2 domain relative to m * c,
-  // acc = sum exp2((S1 - m1) c) (S1 - S2) over raw score differences
-  float m1 = NEG_INF, m2 = NEG_INF, l1 = 0.f, l2 = 0.f, acc = 0.f;
+  // reference maxima of the raw scores, sums in the exp2 domain relative to
+  // m * c, acc = sum exp2((S1 - m1) c) (S1 - S2) over raw score
+  // differences. As in the forward, the rescale is deferred: the reference
+  // maxima move only when a block's maximum exceeds them by more than 2^8
+  // in the exp2 domain, so the weights stay below 2^8 and most blocks skip
+  // the rescale. Each sum runs in two chains (even and odd elements).
+  float m1 = NEG_INF, m2 = NEG_INF;
+  float m1c = 0.f, m2c = 0.f;  // m * c, 0 while m = -inf (no key seen yet)
+  float l1[2] = {0.f, 0.f}, l2[2] = {0.f, 0.f}, acc[2] = {0.f, 0.f};
   const float c = p.scale_log2;
 
-  // One 32-key block at a time (the online update runs per block), so that
-  // only one block's S1^T and S2^T accumulators are live.
+  // One 32-key block at a time, so that only one block's S1^T and S2^T
+  // accumulators are live.
   auto tile_body = [&](int j, const uint8_t* la, const uint8_t* lb, auto mask_tag)
                        __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -199,33 +206,45 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
         t1 = fmaxf(t1, x1[r]);
         t2 = fmaxf(t2, x2[r]);
       }
-      // a row may see no key of this block (causal, diagonal tile): then
-      // its maximum stays as it was; the reference value 0 keeps the
-      // weights below at exp2(-inf) = 0 instead of exp2(-inf + inf)
-      const float n1 = fmaxf(m1, max_halves(t1));
-      const float n2 = fmaxf(m2, max_halves(t2));
-      const float r1 = n1 == NEG_INF ? 0.f : n1;
-      const float r2 = n2 == NEG_INF ? 0.f : n2;
-      const float al1 = fast_exp2((m1 - r1) * c), al2 = fast_exp2((m2 - r2) * c);
-      m1 = n1;
-      m2 = n2;
-      const float r1c = r1 * c, r2c = r2 * c;
-      float sl1 = 0.f, sl2 = 0.f, sa = 0.f;
+      t1 = max_halves(t1);
+      t2 = max_halves(t2);
+      // A row that sees no key of this block (causal, diagonal tile) has
+      // t = -inf and never moves its maximum here; while a row has seen no
+      // key at all its m * c stays 0, so masked weights are exp2(-inf) = 0.
+      const bool g1 = t1 > m1 + p.defer_raw, g2 = t2 > m2 + p.defer_raw;
+      if (__any(g1 || g2)) {
+        // the wave-uniform branch is rare after the first blocks
+        asm volatile("" ::: "memory");
+        if (g1) {
+          const float al = fast_exp2((m1 - t1) * c);  // 0 when m1 = -inf
+          m1 = t1;
+          m1c = t1 * c;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            l1[e] *= al;
+            acc[e] *= al;
+          }
+        }
+        if (g2) {
+          const float al = fast_exp2((m2 - t2) * c);
+          m2 = t2;
+          m2c = t2 * c;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) l2[e] *= al;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p1 = fast_exp2(__builtin_fmaf(x1[r], c, -r1c));
-        const float p2 = fast_exp2(__builtin_fmaf(x2[r], c, -r2c));
+        const float p1 = fast_exp2(__builtin_fmaf(x1[r], c, -m1c));
+        const float p2 = fast_exp2(__builtin_fmaf(x2[r], c, -m2c));
         // the difference of the raw (unmasked, finite) scores; the scale is
         // applied to acc once at the end. Exactly 0 where the two scores are
         // equal.
         const float dx = s1[r] - s2[r];
-        sl1 += p1;
-        sl2 += p2;
-        sa = __builtin_fmaf(p1, dx, sa);
+        l1[r & 1] += p1;
+        l2[r & 1] += p2;
+        acc[r & 1] = __builtin_fmaf(p1, dx, acc[r & 1]);
       }
-      l1 = __builtin_fmaf(l1, al1, sl1);
-      l2 = __builtin_fmaf(l2, al2, sl2);
-      acc = __builtin_fmaf(acc, al1, sa);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -262,20 +281,20 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
   run(j_end, n_kt, std::integral_constant<int, 0>{});
 
   // both halves of the row: add the sums, then KL = acc/l1 + LSE2 - LSE1
-  l1 = sum_halves(l1);
-  l2 = sum_halves(l2);
-  acc = sum_halves(acc);
+  const float L1 = sum_halves(l1[0] + l1[1]);
+  const float L2 = sum_halves(l2[0] + l2[1]);
+  const float A = sum_halves(acc[0] + acc[1]);
   if (hf == 0 && my_q < p.Nq) {
-    const float lse1 = __builtin_fmaf(m1, c, fast_log2(l1)) * kl::kLn2;
-    const float lse2 = __builtin_fmaf(m2, c, fast_log2(l2)) * kl::kLn2;
+    const float lse1 = __builtin_fmaf(m1, c, fast_log2(L1)) * kl::kLn2;
+    const float lse2 = __builtin_fmaf(m2, c, fast_log2(L2)) * kl::kLn2;
     const size_t r = (size_t)bh * p.Nq + my_q;
     p.lse1[r] = lse1;
     p.lse2[r] = lse2;
     // LSE2 - LSE1 from the differences of the maxima and of the log sums,
     // not of the two LSEs (no cancellation of two large values, and exactly
     // 0 for identical distributions)
-    const float dlse = (m2 - m1) * c + (fast_log2(l2) - fast_log2(l1));
-    p.kl[r] = (acc * c / l1 + dlse) * kl::kLn2;
+    const float dlse = (m2 - m1) * c + (fast_log2(L2) - fast_log2(L1));
+    p.kl[r] = (A * c / L1 + dlse) * kl::kLn2;
   }
 }
 
