@@ -459,67 +459,123 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
   const float c = p.scale_log2;
 
+  // One query tile in four MFMA phases, ordered so that the VALU work of
+  // the tile runs between MFMAs that do not depend on it (one wave per SIMD
+  // at d = 128: no other wave would hide it):
+  //   1. S = Q K^T                       (8 MFMAs at d = 128)
+  //   2. dP = dO V^T, with P = exp2(S c - LSE log2 e) computed between them
+  //   3. dV^T += dO^T P, with dS = P o (dP - D) computed between them
+  //   4. dK^T += Q^T dS
+  // Phases 2 and 3 are fenced slots: per MFMA, its LDS operand reads a few
+  // MFMAs ahead and a share of the VALU work.
   auto tile_body = [&](int t, const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld,
                        auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int qt0 = t * BQt;
-    // S = Q K^T and dP = dO V^T (queries on MFMA rows, one key per lane)
+    // LSE and D of this lane's 16 queries (element r is query
+    // qt0 + 16*(r>>3) + 8*hf + (r&7)), read first: they feed phase 2 and 3
+    u32x4 lq4[2 * PK], dq4[2 * PK];
+#pragma unroll
+    for (int ks = 0; ks < PK; ++ks) {
+      const int qr = 16 * ks + 8 * hf;
+      lq4[2 * ks] = *reinterpret_cast<const u32x4*>(ll + qr);
+      lq4[2 * ks + 1] = *reinterpret_cast<const u32x4*>(ll + qr + 4);
+      dq4[2 * ks] = *reinterpret_cast<const u32x4*>(ld + qr);
+      dq4[2 * ks + 1] = *reinterpret_cast<const u32x4*>(ld + qr + 4);
+    }
+    // 1. S = Q K^T (queries on MFMA rows, one key per lane)
     f32x16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
     for (int i = 0; i < DK; ++i) {
       const u32x4 qa = *reinterpret_cast<const u32x4*>(lq + roff[i]);
-      const u32x4 ga = *reinterpret_cast<const u32x4*>(lg + roff[i]);
       s = O_::mfma(qa, kf[i], s);
-      dp = O_::mfma(ga, vf[i], dp);
     }
-    sync::PinReads<0, 2 * DK, 1, 4>::apply();
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * PK, 0);  // LSE and D reads
+    sync::PinReads<0, DK, 1, 4>::apply();
     __builtin_amdgcn_sched_barrier(0);
-    // element r is query qt0 + 16*(r>>3) + 8*hf + (r&7)
-    u32x4 pp[PK], dsp[PK];
+    // 2. dP = dO V^T, and P between its MFMAs: slot n holds MFMA n, the
+    // operand read kA2 MFMAs ahead and P of elements [n*EP2, (n+1)*EP2).
+    // The asm statements on the packed values keep the compiler from sinking
+    // the exponentials to their use in phase 3. Each holds one s_nop: the
+    // compiler counts every asm statement as one wait state when it spaces
+    // an MFMA and a VALU read of its result, so an empty one would leave the
+    // read a wait state short (dP read before its MFMA has written it).
+    constexpr int kA2 = 3;
+    constexpr int EP2 = 16 / DK;  // elements per slot (2 at d = 128, 4 at d = 64)
+    float pr[16];
+    u32x4 pp[PK];
+    {
+      u32x4 gbuf[kA2];
 #pragma unroll
-    for (int ks = 0; ks < PK; ++ks) {
-      const int qr = 16 * ks + 8 * hf;  // first query (tile row) of this lane's 8
-      const u32x4 l_lo = *reinterpret_cast<const u32x4*>(ll + qr);
-      const u32x4 l_hi = *reinterpret_cast<const u32x4*>(ll + qr + 4);
-      const u32x4 d_lo = *reinterpret_cast<const u32x4*>(ld + qr);
-      const u32x4 d_hi = *reinterpret_cast<const u32x4*>(ld + qr + 4);
-      float pv[8], dv8[8];
+      for (int n = 0; n < kA2; ++n) gbuf[n] = *reinterpret_cast<const u32x4*>(lg + roff[n]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t lb = u < 4 ? l_lo[u] : l_hi[u - 4];
-        const uint32_t dbits = u < 4 ? d_lo[u] : d_hi[u - 4];
-        const float lse2 = __builtin_bit_cast(float, lb) * bwd::kLog2e;
-        const float dl = __builtin_bit_cast(float, dbits);
-        const int r = 8 * ks + u;
-        float pr = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
-        if constexpr (MASK) {
-          const int q = qt0 + qr + u;
-          const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
-          pr = vis ? pr : 0.f;
+      for (int n = 0; n < DK; ++n) {
+        const u32x4 ga = gbuf[n % kA2];
+        if (n + kA2 < DK) gbuf[n % kA2] = *reinterpret_cast<const u32x4*>(lg + roff[n + kA2]);
+        dp = O_::mfma(ga, vf[n], dp);
+#pragma unroll
+        for (int r = n * EP2; r < (n + 1) * EP2; ++r) {
+          const uint32_t lb = lq4[r >> 2][r & 3];
+          float x = fast_exp2(__builtin_fmaf(s[r], c, -(__builtin_bit_cast(float, lb) * bwd::kLog2e)));
+          if constexpr (MASK) {
+            const int q = qt0 + 16 * (r >> 3) + 8 * hf + (r & 7);
+            const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
+            x = vis ? x : 0.f;
+          }
+          pr[r] = x;
         }
-        pv[u] = pr;
-        dv8[u] = pr * (dp[r] - dl);
-      }
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        pp[ks][tt] = O_::pack(pv[2 * tt], pv[2 * tt + 1]);
-        dsp[ks][tt] = O_::pack(dv8[2 * tt], dv8[2 * tt + 1]);
+        for (int r = n * EP2; r < (n + 1) * EP2; r += 2) {
+          uint32_t w = O_::pack(pr[r], pr[r + 1]);
+          asm volatile("s_nop 0" : "+v"(w));
+          pp[r >> 3][(r & 7) >> 1] = w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P and dK^T += Q^T dS
+    // 3. dV^T += dO^T P, and dS between its MFMAs: slot j holds MFMA j
+    // (k-step j / DB, head-dim block j % DB), its two transpose reads kA3
+    // MFMAs ahead and dS of elements [j*EP3, (j+1)*EP3).
+    constexpr int EP3 = 16 / (PK * DB);
+    constexpr int kA3 = 2;
+    u32x4 dsp[PK];
+    {
+      auto tr_op = [&](int j) __attribute__((always_inline)) {
+        return bwd::tr_operand(lg + (j / DB) * 16 * ROWB, toff[j % DB][0], toff[j % DB][1]);
+      };
+      u32x4 gbuf3[kA3];
+#pragma unroll
+      for (int j = 0; j < kA3; ++j) gbuf3[j] = tr_op(j);
+#pragma unroll
+      for (int j = 0; j < PK * DB; ++j) {
+        const int ks = j / DB, db = j % DB;
+        const u32x4 ga = gbuf3[j % kA3];
+        if (j + kA3 < PK * DB) gbuf3[j % kA3] = tr_op(j + kA3);
+        dvt[db] = O_::mfma(ga, pp[ks], dvt[db]);
+#pragma unroll
+        for (int r = j * EP3; r < (j + 1) * EP3; r += 2) {
+          // (read as plain integers first: __builtin_bit_cast of a vector
+          // element reads element 0)
+          const uint32_t b0 = dq4[r >> 2][r & 3], b1 = dq4[(r + 1) >> 2][(r + 1) & 3];
+          const float d0 = __builtin_bit_cast(float, b0), d1 = __builtin_bit_cast(float, b1);
+          uint32_t w = O_::pack(pr[r] * (dp[r] - d0), pr[r + 1] * (dp[r + 1] - d1));
+          asm volatile("s_nop 0" : "+v"(w));
+          dsp[r >> 3][(r & 7) >> 1] = w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // 4. dK^T += Q^T dS
 #pragma unroll
     for (int ks = 0; ks < PK; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x4 ga = bwd::tr_operand(lg + ks * 16 * ROWB, toff[db][0], toff[db][1]);
         const u32x4 qa = bwd::tr_operand(lq + ks * 16 * ROWB, toff[db][0], toff[db][1]);
-        dvt[db] = O_::mfma(ga, pp[ks], dvt[db]);
         dkt[db] = O_::mfma(qa, dsp[ks], dkt[db]);
       }
-    sync::PinReads<0, 2 * PK * DB, 2, 4>::apply();
+    sync::PinReads<0, PK * DB, 2, 2>::apply();
   };
   // Steps: one per query tile u = 0 .. n_t-1 (tile t_begin + u), each with
   // one barrier; tile u lives in buffer u & 1. A causal wave has nothing to
