@@ -2,7 +2,10 @@
 
 A step is one mha_fwd call (``--pass fwd``) or one mha_bwd call (``--pass
 bwd``: D, dQ and dK/dV, from the forward's O and LSE computed beforehand)
-over the whole workload, inputs already resident in HBM. Default workload:
+over the whole workload, inputs already resident in HBM. After the W
+warm-up steps, untimed steps run for SETTLE_S seconds (the engine clock
+ramps up under load); then K steps run back to back between two events on
+the launch stream. Default workload:
 B=1, H=8, Nq=Nk=16384, d=128, bf16, causal (the long-sequence small-batch
 regime of the FlashAttention long-sequence post). Prints ONE JSON line.
 
@@ -357,6 +360,61 @@ def cpu_baseline_bwd(w: wl.Workload, qb, kb, vb, gb, target_s: float) -> dict:
     }
 
 
+SETTLE_S = 0.25  # untimed load before the timed region (engine clock ramp)
+
+
+def settle(torch, step, min_s: float = SETTLE_S) -> int:
+    """Untimed launches, in batches of 10, until min_s seconds of load have
+    passed: after the warm-up steps the engine clock is still ramping up (the
+    first hundred launches after idle run a few percent slower than the
+    ones after them). Returns the number of launches."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        n += 10
+    return n
+
+
+def time_steps(torch, stream, step, K: int):
+    """The timed region: K steps back to back between two events recorded on
+    the launch stream, bracketed by device synchronisation. Returns (ms per
+    step, wall seconds)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K, time.perf_counter() - t0
+
+
+def per_launch_events(torch, stream, step, K: int) -> np.ndarray:
+    """Outside the timed region: K launches, each between its own pair of
+    events. An event's release between launches adds a gap of a few
+    microseconds and starts the next launch with flushed caches, so these
+    times are longer than the back-to-back average; reported, not used."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(K):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
+
+
+def launch_fields(ms_per_step: float, per: np.ndarray) -> dict:
+    return {"mean": round(ms_per_step, 5),
+            "per_launch_events": {"mean": round(float(per.mean()), 5),
+                                  "median": round(float(np.median(per)), 5),
+                                  "min": round(float(per.min()), 5)}}
+
+
 def calib_copy(torch, mib: int, device) -> None:
     """Three plain device-to-device copies of ``mib`` MiB: a hardware counter
     of bytes read or written, taken over the same run, is scaled by what it
@@ -392,18 +450,11 @@ def bench_proj(args, torch, mha, w) -> int:
         step()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(K):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])
-    ms = ev[0].elapsed_time(ev[K]) / K
+    n_settle = settle(torch, step)
+    ms, wall = time_steps(torch, stream, step, K)
+    per = per_launch_events(torch, stream, step, K)
     tflops = w.flops / (ms * 1e-3) / 1e12
-    achieved = w.flops / (per.mean() * 1e-3) / 1e12
+    achieved = tflops
     line = {
         "metric": f"{METRIC_PROJ} (B={w.B},Nq={w.Nq},H={w.H},d={w.d},E={w.E}, {w.dtype})",
         "value": round(tflops, 2), "unit": "TFLOP/s",
@@ -415,10 +466,9 @@ def bench_proj(args, torch, mha, w) -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": hbm_traffic(w.name, "proj"), "kernel": "mha_proj_kernel",
-                     "launch_ms": {"mean": round(float(per.mean()), 5),
-                                   "median": round(float(np.median(per)), 5),
-                                   "min": round(float(per.min()), 5)}},
+                     "launch_ms": launch_fields(ms, per)},
         "timed_wall_s": round(wall, 3),
+        "settle_launches": n_settle,
         "kernel_source_sha256_16": kernel_source_hash(KERNEL_SOURCES_PROJ),
         "device": device_info(torch),
     }
@@ -566,32 +616,15 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # timed region: events on the stream the kernel is launched on
+    # untimed settling load, then the timed region: K steps back to back, one
+    # event pair on the launch stream
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(K):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])  # ms
-    total_ms = ev[0].elapsed_time(ev[K])
-    ms_per_step = total_ms / K
-
-    # outside the timed region: the same launches back to back with one event
-    # pair around them (amortised, no event between launches), and launches
-    # each preceded by a write of MALL_FLUSH_MIB MiB (the inputs then come
-    # from HBM, not from the last-level cache)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(K):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    amortised_ms = e0.elapsed_time(e1) / K
+    n_settle = settle(torch, step)
+    ms_per_step, wall = time_steps(torch, stream, step, K)
+    # outside the timed region: each launch between its own events, and
+    # launches each preceded by a write of MALL_FLUSH_MIB MiB (the inputs
+    # then come from HBM, not from the last-level cache)
+    per = per_launch_events(torch, stream, step, K)
     flushed_ms = None
     if args.which == "fwd":
         scratch = torch.empty(MALL_FLUSH_MIB << 18, dtype=torch.float32, device=q.device)
@@ -610,7 +643,7 @@ def main() -> int:
     dev = device_info(torch)
     flops = 2.5 * w.flops if args.which == "bwd" else w.flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (per.mean() * 1e-3) / 1e12
+    achieved = tflops  # per launch: the back-to-back average launch duration
     traffic = hbm_traffic(w.name, args.which)
     srcs = {"fwd": KERNEL_SOURCES, "bwd": KERNEL_SOURCES_BWD, "splitkv": KERNEL_SOURCES_SPLIT,
             "kl": KERNEL_SOURCES_KL}
@@ -619,7 +652,7 @@ def main() -> int:
     if args.which == "splitkv":
         # HBM-bound: the metric is the algorithmic bytes moved per second
         gbs = w.io_bytes / (ms_per_step * 1e-3) / 1e9
-        gbs_launch = w.io_bytes / (per.mean() * 1e-3) / 1e9
+        gbs_launch = gbs
         line = {
             "metric": f"{METRIC_SPLIT} ({shape})",
             "value": round(gbs, 1),
@@ -654,20 +687,17 @@ def main() -> int:
         if io_bytes:
             # algorithmic bytes (Q, K, V read once, O and LSE written once) per second
             roof["algorithmic_bytes"] = io_bytes
-            roof["achieved_gbs"] = round(io_bytes / (per.mean() * 1e-3) / 1e9, 1)
+            roof["achieved_gbs"] = round(io_bytes / (ms_per_step * 1e-3) / 1e9, 1)
             roof["achieved_gbs_frac"] = round(roof["achieved_gbs"] / PEAK_GBS, 4)
             if traffic:
-                roof["traffic_gbs"] = round(traffic / (per.mean() * 1e-3) / 1e9, 1)
+                roof["traffic_gbs"] = round(traffic / (ms_per_step * 1e-3) / 1e9, 1)
         roof.update(sq_counters(w.name, args.which))
         if roof.get("sclk_mhz_under_load") and dev["cus"]:
             # the dense ceiling at the engine clock the counters saw under this load
             pk = dev["cus"] * roof["sclk_mhz_under_load"] * 1e6 * MFMA_FLOP_PER_CLK_PER_CU / 1e12
             roof["peak_at_sclk_under_load"] = round(pk, 1)
             roof["frac_at_sclk_under_load"] = round(achieved / pk, 4)
-    roof["launch_ms"] = {"mean": round(float(per.mean()), 5),
-                         "median": round(float(np.median(per)), 5),
-                         "min": round(float(per.min()), 5),
-                         "amortised_back_to_back": round(amortised_ms, 5)}
+    roof["launch_ms"] = launch_fields(ms_per_step, per)
     if flushed_ms is not None:
         roof["mall_flushed"] = {"flush_mib": MALL_FLUSH_MIB, "launch_ms_median": round(flushed_ms, 5),
                                 "tflops": round(flops / (flushed_ms * 1e-3) / 1e12, 2),
@@ -687,6 +717,7 @@ def main() -> int:
                    "accumulate": "fp32", "flops_per_step": flops},
         "roofline": roof,
         "timed_wall_s": round(wall, 3),
+        "settle_launches": n_settle,
         "kernel_source_sha256_16": kernel_source_hash(srcs[args.which]),
         "device": dev,
     })
