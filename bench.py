@@ -10,20 +10,31 @@ B=1, H=8, Nq=Nk=16384, d=128, bf16, causal (the long-sequence small-batch
 regime of the FlashAttention long-sequence post). Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
-                  [--pass fwd|bwd] [--no-cpu-baseline] [--cpu-seconds S]
-                  [--calib-copy-mib M]
+                  [--pass fwd|bwd|splitkv|kl|proj] [--no-cpu-baseline]
+                  [--cpu-seconds S] [--calib-copy-mib M] [--counters]
+
+With --counters, rocprofv3 counter passes over this script run first (as
+child processes, before this process touches the GPU) and their HBM bytes,
+MFMA busy fraction and engine clock are reported live in the line;
+otherwise those fields come from the committed profiles/ summaries while
+the kernel sources match them.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
 import hashlib
 import re
 import json
 import math
 import os
 import resource
+import shutil
+import subprocess
 import sys
+import tempfile
 import time
 from concurrent.futures import ThreadPoolExecutor
 
@@ -378,6 +389,27 @@ def settle(torch, step, min_s: float = SETTLE_S) -> int:
     return n
 
 
+def apply_live(roof: dict, live, flops: float, ms_per_step: float, dev: dict) -> None:
+    """Put live counter results (--counters) into the roofline object, in
+    place of the committed summaries' figures."""
+    if not live:
+        return
+    roof["counters_live"] = live
+    if "error" in live:
+        return
+    roof["traffic"] = live["hbm_bytes_per_step"]
+    roof["traffic_source"] = "live counters"
+    roof["traffic_gbs"] = round(live["hbm_bytes_per_step"] / (ms_per_step * 1e-3) / 1e9, 1)
+    for src, dst in (("mfma_busy", "mfma_busy"), ("sclk_mhz", "sclk_mhz_under_load"),
+                     ("mfma_busy_lower_bound", "mfma_busy_lower_bound")):
+        if src in live:
+            roof[dst] = live[src]
+    if roof.get("sclk_mhz_under_load") and dev.get("cus") and roof.get("unit") == "TFLOP/s":
+        pk = dev["cus"] * roof["sclk_mhz_under_load"] * 1e6 * MFMA_FLOP_PER_CLK_PER_CU / 1e12
+        roof["peak_at_sclk_under_load"] = round(pk, 1)
+        roof["frac_at_sclk_under_load"] = round(flops / (ms_per_step * 1e-3) / 1e12 / pk, 4)
+
+
 def time_steps(torch, stream, step, K: int):
     """The timed region: K steps back to back between two events recorded on
     the launch stream, bracketed by device synchronisation. Returns (ms per
@@ -429,7 +461,7 @@ def calib_copy(torch, mib: int, device) -> None:
           file=sys.stderr, flush=True)
 
 
-def bench_proj(args, torch, mha, w) -> int:
+def bench_proj(args, torch, mha, w, live=None) -> int:
     """The output-projection pass (its own workload type: O, W, bias)."""
     ob, wb, bb = wl.make_proj_inputs(w)
     o, wt, b = (to_device(torch, x, w.dtype) for x in (ob, wb, bb))
@@ -472,6 +504,7 @@ def bench_proj(args, torch, mha, w) -> int:
         "kernel_source_sha256_16": kernel_source_hash(KERNEL_SOURCES_PROJ),
         "device": device_info(torch),
     }
+    apply_live(line["roofline"], live, w.flops, ms, line["device"])
     if not args.no_cpu_baseline:
         print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
               flush=True)
@@ -507,6 +540,114 @@ def cpu_baseline_proj(w, ob, wb, bb, target_s: float) -> dict:
             "seconds": t}
 
 
+# ---- live counters (--counters) ----------------------------------------------
+# rocprofv3 counter passes over this same script, each a child process of its
+# own started before this process touches the GPU: FETCH_SIZE and WRITE_SIZE
+# (HBM bytes, scaled by what they read for three plain 512 MiB device copies
+# in the same run) and SQ/GRBM counters (MFMA busy cycles and the engine
+# clock). The timed launches of a child are found from the settle count it
+# prints; their mean per step is reported.
+STEP_KERNELS = {"fwd": ["mha_fwd_kernel"],
+                "bwd": ["mha_bwd_delta_kernel", "mha_bwd_dq_kernel", "mha_bwd_dkdv_kernel"],
+                "splitkv": ["mha_split_partial_kernel", "mha_split_merge_kernel"],
+                "kl": ["mha_kl_kernel"], "proj": ["mha_proj_kernel"]}
+LIVE_SQ = ["SQ_WAVES", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+N_XCD, N_SIMD = 8, 1024
+CALIB_MIB = 512
+
+
+def _kernel_key(name: str):
+    m = re.search(r"(mha_\w+?_kernel|__amd_rocclr_copyBuffer)", name)
+    return m.group(1) if m else None
+
+
+def _pmc_run(rocprof, counters, which, workload, steps, calib, workdir, timeout_s=240):
+    """One rocprofv3 --pmc pass over a child bench run; returns (child's JSON
+    line, dispatches in order as dicts of kernel key and counter values)."""
+    out = tempfile.mkdtemp(prefix="pmc_", dir=workdir)
+    child = [sys.executable, os.path.abspath(__file__), "--pass", which, "--workload", workload,
+             "--steps", str(steps), "--warmup", "1", "--no-cpu-baseline"]
+    if calib:
+        child += ["--calib-copy-mib", str(CALIB_MIB)]
+    cmd = [rocprof, "--pmc", *counters, "--output-format", "csv", "-d", out, "-o", "p", "--", *child]
+    print("bench.py: " + " ".join(cmd), file=sys.stderr, flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout_s)
+    line = None
+    for ln in res.stdout.splitlines():
+        if ln.startswith("{") and '"metric"' in ln:
+            line = json.loads(ln)
+    files = glob.glob(os.path.join(out, "**", "*counter_collection.csv"), recursive=True)
+    if res.returncode != 0 or line is None or not files:
+        raise RuntimeError(f"counter pass {counters} failed (rc {res.returncode}): "
+                           + res.stderr[-500:])
+    disp = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            e = disp.setdefault(int(r["Dispatch_Id"]), {"key": _kernel_key(r["Kernel_Name"]),
+                                                         "start": int(r["Start_Timestamp"]),
+                                                         "end": int(r["End_Timestamp"])})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return line, [disp[k] for k in sorted(disp)], cmd
+
+
+def _timed(dispatches, key, line, steps):
+    """The child's timed launches of kernel `key` (one per step)."""
+    ds = [d for d in dispatches if d["key"] == key]
+    first = 1 + int(line.get("settle_launches", 0))
+    return ds[first:first + steps]
+
+
+def live_counters(which: str, workload: str) -> dict:
+    rocprof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if not os.path.exists(rocprof):
+        raise RuntimeError("rocprofv3 not found")
+    steps = 3
+    work = tempfile.mkdtemp(prefix="bench_counters_")
+    try:
+        out = {"source": "live rocprofv3 counter passes", "timed_launches": steps, "commands": []}
+        per = {}
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            line, ds, cmd = _pmc_run(rocprof, [ctr], which, workload, steps, True, work)
+            out["commands"].append(" ".join(cmd[cmd.index("--pmc"):]))
+            copies = [d[ctr] for d in ds if d["key"] == "__amd_rocclr_copyBuffer"
+                      and d[ctr] > 0.4 * CALIB_MIB * 1024]
+            factor = CALIB_MIB * 1024 / (sum(copies) / len(copies))
+            tot = 0.0
+            for k in STEP_KERNELS[which]:
+                t = _timed(ds, k, line, steps)
+                tot += sum(d[ctr] for d in t) / len(t) * 1024 * factor
+            per[ctr] = tot
+            out[f"{ctr.lower()}_calibration_factor"] = round(factor, 4)
+        out["fetch_bytes_per_step"] = round(per["FETCH_SIZE"])
+        out["write_bytes_per_step"] = round(per["WRITE_SIZE"])
+        out["hbm_bytes_per_step"] = round(per["FETCH_SIZE"] + per["WRITE_SIZE"])
+        if which != "splitkv":
+            line, ds, cmd = _pmc_run(rocprof, LIVE_SQ, which, workload, steps, False, work)
+            out["commands"].append(" ".join(cmd[cmd.index("--pmc"):]))
+            kern = {}
+            for k in STEP_KERNELS[which]:
+                t = _timed(ds, k, line, steps)
+                dur = sum(d["end"] - d["start"] for d in t) / len(t)
+                busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in t) / len(t) / N_SIMD
+                grbm = sum(d["GRBM_GUI_ACTIVE"] for d in t) / len(t) / N_XCD
+                e = {"dispatch_us": round(dur / 1e3, 1), "mfma_busy_cycles_per_simd": round(busy)}
+                if dur >= 1e5:  # GRBM also counts the dispatch's start and end
+                    e["mfma_busy"] = round(busy / grbm, 4)
+                    e["sclk_mhz"] = round(grbm / dur * 1e3)
+                else:
+                    e["mfma_busy_lower_bound"] = round(busy / grbm, 4)
+                kern[k] = e
+            out["kernels"] = kern
+            dom = max(kern, key=lambda k: kern[k]["dispatch_us"])
+            out["dominant_kernel"] = dom
+            for f in ("mfma_busy", "sclk_mhz", "mfma_busy_lower_bound"):
+                if f in kern[dom]:
+                    out[f] = kern[dom][f]
+        return out
+    finally:
+        shutil.rmtree(work, ignore_errors=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -523,13 +664,26 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--counters", action="store_true",
+                    help="also run rocprofv3 counter passes (HBM bytes, MFMA busy, engine "
+                         "clock) over this script first and report them live")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the forward shards over heads with no communication; see DESIGN.md)",
               file=sys.stderr)
         return 2
+
+    live = None
+    if args.counters:
+        # child processes, started before this process touches the GPU
+        wname = args.workload or {"splitkv": "decode", "kl": "kl_long",
+                                  "proj": "proj_long"}.get(args.which, "long_causal")
+        try:
+            live = live_counters(args.which, wname)
+        except (RuntimeError, subprocess.TimeoutExpired, ZeroDivisionError, IndexError) as e:
+            live = {"error": str(e)[-300:]}
 
     import torch
 
@@ -542,7 +696,7 @@ def main() -> int:
     name = args.workload or {"splitkv": "decode", "kl": "kl_long",
                              "proj": "proj_long"}.get(args.which, "long_causal")
     if args.which == "proj":
-        return bench_proj(args, torch, mha, wl.PROJ_WORKLOADS[name])
+        return bench_proj(args, torch, mha, wl.PROJ_WORKLOADS[name], live)
     w = wl.WORKLOADS.get(name) or wl.DECODE_WORKLOADS.get(name) or wl.KL_WORKLOADS[name]
     if args.which == "kl":
         qb, kb, q2b, k2b = wl.make_kl_inputs(w)
@@ -692,6 +846,8 @@ def main() -> int:
             if traffic:
                 roof["traffic_gbs"] = round(traffic / (ms_per_step * 1e-3) / 1e9, 1)
         roof.update(sq_counters(w.name, args.which))
+        if traffic:
+            roof["traffic_source"] = "committed summary (kernel sources match)"
         if roof.get("sclk_mhz_under_load") and dev["cus"]:
             # the dense ceiling at the engine clock the counters saw under this load
             pk = dev["cus"] * roof["sclk_mhz_under_load"] * 1e6 * MFMA_FLOP_PER_CLK_PER_CU / 1e12
@@ -721,6 +877,7 @@ def main() -> int:
         "kernel_source_sha256_16": kernel_source_hash(srcs[args.which]),
         "device": dev,
     })
+    apply_live(roof, live, flops, ms_per_step, dev)
     if not args.no_cpu_baseline:
         print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
               flush=True)
