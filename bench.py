@@ -580,18 +580,26 @@ def _pmc_run(rocprof, counters, which, workload, steps, calib, workdir, timeout_
     if res.returncode != 0 or line is None or not files:
         raise RuntimeError(f"counter pass {counters} failed (rc {res.returncode}): "
                            + res.stderr[-500:])
+    return line, read_counter_csv(files[0]), cmd
+
+
+def read_counter_csv(path: str) -> list:
+    """rocprofv3 counter_collection.csv -> one dict per dispatch, in dispatch
+    order: kernel key, start and end timestamps (ns) and each counter summed
+    over the rows of that dispatch."""
     disp = {}
-    with open(files[0]) as f:
+    with open(path) as f:
         for r in csv.DictReader(f):
             e = disp.setdefault(int(r["Dispatch_Id"]), {"key": _kernel_key(r["Kernel_Name"]),
                                                          "start": int(r["Start_Timestamp"]),
                                                          "end": int(r["End_Timestamp"])})
             e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    return line, [disp[k] for k in sorted(disp)], cmd
+    return [disp[k] for k in sorted(disp)]
 
 
 def _timed(dispatches, key, line, steps):
-    """The child's timed launches of kernel `key` (one per step)."""
+    """The child's timed launches of kernel `key` (one per step): after its
+    one warm-up launch and its settling launches."""
     ds = [d for d in dispatches if d["key"] == key]
     first = 1 + int(line.get("settle_launches", 0))
     return ds[first:first + steps]
