@@ -82,6 +82,25 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst,
                                            4, voffset, 0, 0, 0);
 }
 
+// Calls f(std::integral_constant<int, I>) for I = B, ..., E - 1 in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Element ranges of VALU work spread over fenced slots: slot j of a tile
+// handles elements [lo(j), lo(j + 1)) of a 16-element task spread evenly
+// over slots [FIRST, FIRST + COUNT). A packed pair may straddle two slots.
+template <int FIRST, int COUNT>
+struct Spread {
+  static constexpr __host__ __device__ int lo(int j) {
+    return j <= FIRST ? 0 : j >= FIRST + COUNT ? 16 : (16 * (j - FIRST)) / COUNT;
+  }
+};
+
 }  // namespace bwd
 
 // ---- D = rowsum(dO o O) ------------------------------------------------------
@@ -394,7 +413,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   const int kw0 = k0 + wave * 32;
   const int my_k = kw0 + ln;
 
-  // K and V fragments of this wave's keys (B operands), read once
+  // K and -V fragments of this wave's keys (B operands), read once
   u32x4 kf[DK], vf[DK];
   if (my_k < p.Nk) {
     const uint16_t* krow = p.k + kvo + (size_t)my_k * rs + 8 * hf;
@@ -403,6 +422,9 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     for (int i = 0; i < DK; ++i) {
       kf[i] = *reinterpret_cast<const u32x4*>(krow + 16 * i);
       vf[i] = *reinterpret_cast<const u32x4*>(vrow + 16 * i);
+      // negated (sign bits flipped, exact): the dP MFMAs then compute D - dP
+#pragma unroll
+      for (int w = 0; w < 4; ++w) vf[i][w] ^= 0x80008000u;
     }
   } else {
 #pragma unroll
@@ -459,21 +481,49 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
   const float c = p.scale_log2;
 
-  // One query tile in four MFMA phases, ordered so that the VALU work of
-  // the tile runs between MFMAs that do not depend on it (one wave per SIMD
-  // at d = 128: no other wave would hide it):
-  //   1. S = Q K^T                       (8 MFMAs at d = 128)
-  //   2. dP = dO V^T, with P = exp2(S c - LSE log2 e) computed between them
-  //   3. dV^T += dO^T P, with dS = P o (dP - D) computed between them
-  //   4. dK^T += Q^T dS
-  // Phases 2 and 3 are fenced slots: per MFMA, its LDS operand reads a few
-  // MFMAs ahead and a share of the VALU work.
+  // One query tile: 4 MFMA phases, 32 MFMAs at d = 128, run as one sequence
+  // of fenced slots. Slot j holds MFMA j, the LDS read of the operand of
+  // MFMA j + kA (one operand ring across all phases, so that no phase starts
+  // on a read just issued) and a share of the VALU work, spread so that no
+  // slot holds much more than the MFMA covers (one wave per SIMD at
+  // d = 128: no other wave would hide it):
+  //   1. S = Q K^T                (N1 MFMAs)   VALU: -LSE log2 e
+  //   2. dP' = D - dO V^T         (N2 MFMAs)   VALU: P = exp2(S c - LSE log2 e),
+  //   3. dV^T += dO^T P           (N3 MFMAs)         spread over 2 and half of 3
+  //   4. -dK^T += Q^T (P o dP')   (N4 MFMAs)   VALU: -dS = P o dP', spread over
+  //                                                  the rest of 3 and half of 4
+  // dP' starts from D (the accumulator input of its first MFMA) and takes
+  // the negated V fragments, so -dS is one product per element; the sign
+  // comes back when dK is stored. Operands: Q rows and dO rows (phases 1,
+  // 2) by row reads of the swizzled tiles, dO^T and Q^T (phases 3, 4) by
+  // transpose reads.
+  // The slots are generated at compile time (static_for, if constexpr), so
+  // the code of each is straight-line from the start: with a run-time slot
+  // index the optimiser moved MFMAs of the rolled loop several slots late.
+  // The asm statements on the values computed in a slot keep the compiler
+  // from sinking that arithmetic to its use in a later slot. Each holds one
+  // s_nop: the compiler counts every asm statement as one wait state when it
+  // spaces an MFMA and a VALU read of its result, so an empty one would
+  // leave such a read a wait state short.
   auto tile_body = [&](int t, const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld,
                        auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int N1 = DK, N2 = DK, N3 = PK * DB, N4 = PK * DB;
+    constexpr int NM = N1 + N2 + N3 + N4;
+    constexpr int kA = bwd::kDkdvAhead;
+    constexpr int EP1 = 16 / N1;  // -LSE log2 e values per phase-1 slot
+    static_assert(EP1 % 2 == 0, "pairs per slot");
+    // P over the N2 + N3/2 - 1 slots from N1 on, each half done before the
+    // dV MFMAs that take it; -dS over the slots after, up to the middle of
+    // phase 4, each half done before the dK MFMAs that take it
+    using SpreadP = bwd::Spread<N1, N2 + N3 / 2 - 1>;
+    using SpreadD = bwd::Spread<N1 + N2 + N3 / 2 - 1, N3 / 2 + N4 / 2 + 1>;
+    static_assert(SpreadP::lo(N1 + N2) >= 8 && SpreadP::lo(N1 + N2 + N3 / 2) == 16, "P in time");
+    static_assert(SpreadD::lo(N1 + N2 + N3) >= 8 && SpreadD::lo(N1 + N2 + N3 + N4 / 2) == 16,
+                  "dS in time");
     const int qt0 = t * BQt;
     // LSE and D of this lane's 16 queries (element r is query
-    // qt0 + 16*(r>>3) + 8*hf + (r&7)), read first: they feed phase 2 and 3
+    // qt0 + 16*(r>>3) + 8*hf + (r&7)), read first: they feed phases 1 and 2
     u32x4 lq4[2 * PK], dq4[2 * PK];
 #pragma unroll
     for (int ks = 0; ks < PK; ++ks) {
@@ -483,99 +533,96 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
       dq4[2 * ks] = *reinterpret_cast<const u32x4*>(ld + qr);
       dq4[2 * ks + 1] = *reinterpret_cast<const u32x4*>(ld + qr + 4);
     }
-    // 1. S = Q K^T (queries on MFMA rows, one key per lane)
+    auto operand = [&](auto jt) __attribute__((always_inline)) -> u32x4 {
+      constexpr int j = decltype(jt)::value;
+      if constexpr (j < N1) {
+        return *reinterpret_cast<const u32x4*>(lq + roff[j]);
+      } else if constexpr (j < N1 + N2) {
+        return *reinterpret_cast<const u32x4*>(lg + roff[j - N1]);
+      } else {
+        constexpr bool dv_phase = j < N1 + N2 + N3;
+        constexpr int m = dv_phase ? j - N1 - N2 : j - N1 - N2 - N3;
+        return bwd::tr_operand((dv_phase ? lg : lq) + (m / DB) * 16 * ROWB, toff[m % DB][0],
+                               toff[m % DB][1]);
+      }
+    };
+    u32x4 ring[kA];
+    bwd::static_for<0, kA>([&](auto jt) __attribute__((always_inline)) {
+      ring[decltype(jt)::value] = operand(jt);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+
     f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-    for (int i = 0; i < DK; ++i) {
-      const u32x4 qa = *reinterpret_cast<const u32x4*>(lq + roff[i]);
-      s = O_::mfma(qa, kf[i], s);
+    for (int r = 0; r < 16; ++r) {
+      // (read as plain integers first: __builtin_bit_cast of a vector
+      // element reads element 0)
+      const uint32_t b = dq4[r >> 2][r & 3];
+      s[r] = 0.f;
+      dp[r] = __builtin_bit_cast(float, b);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * PK, 0);  // LSE and D reads
-    sync::PinReads<0, DK, 1, 4>::apply();
-    __builtin_amdgcn_sched_barrier(0);
-    // 2. dP = dO V^T, and P between its MFMAs: slot n holds MFMA n, the
-    // operand read kA2 MFMAs ahead and P of elements [n*EP2, (n+1)*EP2).
-    // The asm statements on the packed values keep the compiler from sinking
-    // the exponentials to their use in phase 3. Each holds one s_nop: the
-    // compiler counts every asm statement as one wait state when it spaces
-    // an MFMA and a VALU read of its result, so an empty one would leave the
-    // read a wait state short (dP read before its MFMA has written it).
-    constexpr int kA2 = 3;
-    constexpr int EP2 = 16 / DK;  // elements per slot (2 at d = 128, 4 at d = 64)
-    float pr[16];
-    u32x4 pp[PK];
-    {
-      u32x4 gbuf[kA2];
-#pragma unroll
-      for (int n = 0; n < kA2; ++n) gbuf[n] = *reinterpret_cast<const u32x4*>(lg + roff[n]);
-#pragma unroll
-      for (int n = 0; n < DK; ++n) {
-        const u32x4 ga = gbuf[n % kA2];
-        if (n + kA2 < DK) gbuf[n % kA2] = *reinterpret_cast<const u32x4*>(lg + roff[n + kA2]);
-        dp = O_::mfma(ga, vf[n], dp);
-#pragma unroll
-        for (int r = n * EP2; r < (n + 1) * EP2; ++r) {
-          const uint32_t lb = lq4[r >> 2][r & 3];
-          float x = fast_exp2(__builtin_fmaf(s[r], c, -(__builtin_bit_cast(float, lb) * bwd::kLog2e)));
-          if constexpr (MASK) {
-            const int q = qt0 + 16 * (r >> 3) + 8 * hf + (r & 7);
-            const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
-            x = vis ? x : 0.f;
-          }
-          pr[r] = x;
+    float nl[16], pr[16], nds[16];
+    u32x4 pp[PK], dsp[PK];
+    bwd::static_for<0, NM>([&](auto jt) __attribute__((always_inline)) {
+      constexpr int j = decltype(jt)::value;
+      const u32x4 a = ring[j % kA];
+      if constexpr (j + kA < NM) ring[j % kA] = operand(std::integral_constant<int, j + kA>{});
+      if constexpr (j < N1) {
+        s = O_::mfma(a, kf[j], s);
+      } else if constexpr (j < N1 + N2) {
+        dp = O_::mfma(a, vf[j - N1], dp);
+      } else if constexpr (j < N1 + N2 + N3) {
+        constexpr int m = j - N1 - N2;
+        dvt[m % DB] = O_::mfma(a, pp[m / DB], dvt[m % DB]);
+      } else {
+        constexpr int m = j - N1 - N2 - N3;
+        dkt[m % DB] = O_::mfma(a, dsp[m / DB], dkt[m % DB]);
+      }
+      // exponent offsets of elements [j*EP1, (j+1)*EP1)
+      if constexpr (j < N1) {
+        bwd::static_for<0, EP1 / 2>([&](auto it) __attribute__((always_inline)) {
+          constexpr int r = j * EP1 + 2 * decltype(it)::value;
+          const uint32_t b0 = lq4[r >> 2][r & 3], b1 = lq4[(r + 1) >> 2][(r + 1) & 3];
+          float x0 = __builtin_bit_cast(float, b0) * -bwd::kLog2e;
+          float x1 = __builtin_bit_cast(float, b1) * -bwd::kLog2e;
+          asm volatile("s_nop 0" : "+v"(x0), "+v"(x1));
+          nl[r] = x0;
+          nl[r + 1] = x1;
+        });
+      }
+      // P of elements [SpreadP::lo(j), SpreadP::lo(j + 1)), packed in pairs
+      bwd::static_for<SpreadP::lo(j), SpreadP::lo(j + 1)>([&](auto rt) __attribute__((always_inline)) {
+        constexpr int r = decltype(rt)::value;
+        float x = fast_exp2(__builtin_fmaf(s[r], c, nl[r]));
+        if constexpr (MASK) {
+          const int q = qt0 + 16 * (r >> 3) + 8 * hf + (r & 7);
+          const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
+          x = vis ? x : 0.f;
         }
-#pragma unroll
-        for (int r = n * EP2; r < (n + 1) * EP2; r += 2) {
-          uint32_t w = O_::pack(pr[r], pr[r + 1]);
+        if constexpr (r & 1) {
+          uint32_t w = O_::pack(pr[r - 1], x);
           asm volatile("s_nop 0" : "+v"(w));
           pp[r >> 3][(r & 7) >> 1] = w;
+        } else if constexpr (r + 1 == SpreadP::lo(j + 1)) {
+          asm volatile("s_nop 0" : "+v"(x));  // its pair is packed in a later slot
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // 3. dV^T += dO^T P, and dS between its MFMAs: slot j holds MFMA j
-    // (k-step j / DB, head-dim block j % DB), its two transpose reads kA3
-    // MFMAs ahead and dS of elements [j*EP3, (j+1)*EP3).
-    constexpr int EP3 = 16 / (PK * DB);
-    constexpr int kA3 = 2;
-    u32x4 dsp[PK];
-    {
-      auto tr_op = [&](int j) __attribute__((always_inline)) {
-        return bwd::tr_operand(lg + (j / DB) * 16 * ROWB, toff[j % DB][0], toff[j % DB][1]);
-      };
-      u32x4 gbuf3[kA3];
-#pragma unroll
-      for (int j = 0; j < kA3; ++j) gbuf3[j] = tr_op(j);
-#pragma unroll
-      for (int j = 0; j < PK * DB; ++j) {
-        const int ks = j / DB, db = j % DB;
-        const u32x4 ga = gbuf3[j % kA3];
-        if (j + kA3 < PK * DB) gbuf3[j % kA3] = tr_op(j + kA3);
-        dvt[db] = O_::mfma(ga, pp[ks], dvt[db]);
-#pragma unroll
-        for (int r = j * EP3; r < (j + 1) * EP3; r += 2) {
-          // (read as plain integers first: __builtin_bit_cast of a vector
-          // element reads element 0)
-          const uint32_t b0 = dq4[r >> 2][r & 3], b1 = dq4[(r + 1) >> 2][(r + 1) & 3];
-          const float d0 = __builtin_bit_cast(float, b0), d1 = __builtin_bit_cast(float, b1);
-          uint32_t w = O_::pack(pr[r] * (dp[r] - d0), pr[r + 1] * (dp[r + 1] - d1));
+        pr[r] = x;
+      });
+      // -dS of elements [SpreadD::lo(j), SpreadD::lo(j + 1)), packed in pairs
+      bwd::static_for<SpreadD::lo(j), SpreadD::lo(j + 1)>([&](auto rt) __attribute__((always_inline)) {
+        constexpr int r = decltype(rt)::value;
+        float y = pr[r] * dp[r];
+        if constexpr (r & 1) {
+          uint32_t w = O_::pack(nds[r - 1], y);
           asm volatile("s_nop 0" : "+v"(w));
           dsp[r >> 3][(r & 7) >> 1] = w;
+        } else if constexpr (r + 1 == SpreadD::lo(j + 1)) {
+          asm volatile("s_nop 0" : "+v"(y));
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // 4. dK^T += Q^T dS
-#pragma unroll
-    for (int ks = 0; ks < PK; ++ks)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4 qa = bwd::tr_operand(lq + ks * 16 * ROWB, toff[db][0], toff[db][1]);
-        dkt[db] = O_::mfma(qa, dsp[ks], dkt[db]);
-      }
-    sync::PinReads<0, PK * DB, 2, 2>::apply();
+        nds[r] = y;
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   // Steps: one per query tile u = 0 .. n_t-1 (tile t_begin + u), each with
   // one barrier; tile u lives in buffer u & 1. A causal wave has nothing to
@@ -637,7 +684,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     const auto out_v = make_rsrc(p.dv + kvo + (size_t)k0 * rs, range);
     uint8_t* const slot = wave == 0 ? lds_q0 : wave == 1 ? lds_q1 : wave == 2 ? lds_g0 : lds_g1;
     const uint32_t gbase = (uint32_t)(wave * 32) * row_bytes;
-    store_rows<O_, D>(dkt, p.scale, slot, out_k, gbase, row_bytes, lane);
+    store_rows<O_, D>(dkt, -p.scale, slot, out_k, gbase, row_bytes, lane);  // dkt holds -dK^T
     store_rows<O_, D>(dvt, 1.f, slot, out_v, gbase, row_bytes, lane);
   }
 }
