@@ -442,7 +442,8 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ bwd::t_swz<D>(row));
   }
   // copies per wave per tile: NCPW each of Q and dO, plus LSE on wave 0 and
-  // D on wave 1
+  // D on wave 1 (their rows of this (b, h), chosen once)
+  const float* const lsd_src = (wave == 0 ? p.lse : p.delta) + (size_t)bh * p.Nq;
   auto issue = [&](int t, uint8_t* lq, uint8_t* lg, float* ll, float* ld) __attribute__((always_inline)) {
     const int nvalid = min(BQt, p.Nq - t * BQt);
     const uint32_t bytes = (uint32_t)(nvalid - 1) * row_bytes + ROWB;
@@ -452,12 +453,9 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     for (int c = 0; c < NCPW; ++c) dma16(rq, lq + (c * NW + wave) * 1024, c_off[c]);
 #pragma unroll
     for (int c = 0; c < NCPW; ++c) dma16(rg, lg + (c * NW + wave) * 1024, c_off[c]);
-    if (wave == 0) {
-      const auto rl = make_rsrc(p.lse + (size_t)bh * p.Nq + t * BQt, (uint32_t)nvalid * 4);
-      bwd::dma4(rl, reinterpret_cast<uint8_t*>(ll), 4 * lane);
-    } else if (wave == 1) {
-      const auto rd = make_rsrc(p.delta + (size_t)bh * p.Nq + t * BQt, (uint32_t)nvalid * 4);
-      bwd::dma4(rd, reinterpret_cast<uint8_t*>(ld), 4 * lane);
+    if (wave < 2) {
+      const auto rl = make_rsrc(lsd_src + t * BQt, (uint32_t)nvalid * 4);
+      bwd::dma4(rl, reinterpret_cast<uint8_t*>(wave == 0 ? ll : ld), 4 * lane);
     }
   };
 
@@ -506,7 +504,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   // spaces an MFMA and a VALU read of its result, so an empty one would
   // leave such a read a wait state short.
   auto tile_body = [&](int t, const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld,
-                       auto mask_tag) __attribute__((always_inline)) {
+                       auto mask_tag, auto&& next) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int N1 = DK, N2 = DK, N3 = PK * DB, N4 = PK * DB;
     constexpr int NM = N1 + N2 + N3 + N4;
@@ -569,6 +567,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
       if constexpr (j + kA < NM) ring[j % kA] = operand(std::integral_constant<int, j + kA>{});
       if constexpr (j < N1) {
         s = O_::mfma(a, kf[j], s);
+        if constexpr (j == 0) next();  // the next tile's copies, once this tile's reads are out
       } else if constexpr (j < N1 + N2) {
         dp = O_::mfma(a, vf[j - N1], dp);
       } else if constexpr (j < N1 + N2 + N3) {
@@ -641,14 +640,18 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     const int t = t_begin + u;
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
     sync::bare_barrier();
-    if (u + 1 < n_t) {
-      if constexpr (P == 0) issue(t + 1, lds_q1, lds_g1, lds_l1, lds_d1);
-      else issue(t + 1, lds_q0, lds_g0, lds_l0, lds_d0);
-    }
+    auto next = [&]() __attribute__((always_inline)) {
+      if (u + 1 < n_t) {
+        if constexpr (P == 0) issue(t + 1, lds_q1, lds_g1, lds_l1, lds_d1);
+        else issue(t + 1, lds_q0, lds_g0, lds_l0, lds_d0);
+      }
+    };
     if constexpr (MODE != 0) {
       using M = std::integral_constant<bool, MODE == 1>;
-      if constexpr (P == 0) tile_body(t, lds_q0, lds_g0, lds_l0, lds_d0, M{});
-      else tile_body(t, lds_q1, lds_g1, lds_l1, lds_d1, M{});
+      if constexpr (P == 0) tile_body(t, lds_q0, lds_g0, lds_l0, lds_d0, M{}, next);
+      else tile_body(t, lds_q1, lds_g1, lds_l1, lds_d1, M{}, next);
+    } else {
+      next();
     }
   };
   using Even = std::integral_constant<int, 0>;
