@@ -375,16 +375,40 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   constexpr int NCPW = TILEB / 1024 / NW;
   static_assert(NCPW >= 1 && (NW * RPI) % 16 == 0, "copy layout");
 
+  // Q and dO tiles, three buffers of each. Separate objects: the compiler
+  // then knows that a copy into one buffer does not write another, and
+  // inserts no wait for the copies before reading a different buffer.
   __shared__ __attribute__((aligned(1024))) uint8_t lds_q0[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_q1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_q2[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_g0[TILEB];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_g1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_g2[TILEB];
   // LSE (copied by wave 0) and D (wave 1) of the tile's queries: one 256-byte
   // copy each, of which the first 128 bytes are the 32 values
   __shared__ __attribute__((aligned(256))) float lds_l0[64];
   __shared__ __attribute__((aligned(256))) float lds_l1[64];
+  __shared__ __attribute__((aligned(256))) float lds_l2[64];
   __shared__ __attribute__((aligned(256))) float lds_d0[64];
   __shared__ __attribute__((aligned(256))) float lds_d1[64];
+  __shared__ __attribute__((aligned(256))) float lds_d2[64];
+  // buffer i (compile-time) of each kind
+  auto bq = [&](auto it) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int i = decltype(it)::value;
+    return i == 0 ? lds_q0 : i == 1 ? lds_q1 : lds_q2;
+  };
+  auto bg = [&](auto it) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int i = decltype(it)::value;
+    return i == 0 ? lds_g0 : i == 1 ? lds_g1 : lds_g2;
+  };
+  auto bl = [&](auto it) __attribute__((always_inline)) -> float* {
+    constexpr int i = decltype(it)::value;
+    return i == 0 ? lds_l0 : i == 1 ? lds_l1 : lds_l2;
+  };
+  auto bd = [&](auto it) __attribute__((always_inline)) -> float* {
+    constexpr int i = decltype(it)::value;
+    return i == 0 ? lds_d0 : i == 1 ? lds_d1 : lds_d2;
+  };
 
   // work item: (batch, head, key block), a head's blocks on one XCD
   const int lin = blockIdx.x;
@@ -481,10 +505,10 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
 
   // One query tile: 4 MFMA phases, 32 MFMAs at d = 128, run as one sequence
   // of fenced slots. Slot j holds MFMA j, the LDS read of the operand of
-  // MFMA j + kA (one operand ring across all phases, so that no phase starts
-  // on a read just issued) and a share of the VALU work, spread so that no
-  // slot holds much more than the MFMA covers (one wave per SIMD at
-  // d = 128: no other wave would hide it):
+  // MFMA j + kA (one operand ring across all phases and on into the next
+  // tile) and a share of the VALU work, spread so that no slot holds much
+  // more than the MFMA covers (one wave per SIMD at d = 128: no other wave
+  // would hide it):
   //   1. S = Q K^T                (N1 MFMAs)   VALU: -LSE log2 e
   //   2. dP' = D - dO V^T         (N2 MFMAs)   VALU: P = exp2(S c - LSE log2 e),
   //   3. dV^T += dO^T P           (N3 MFMAs)         spread over 2 and half of 3
@@ -494,7 +518,10 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   // the negated V fragments, so -dS is one product per element; the sign
   // comes back when dK is stored. Operands: Q rows and dO rows (phases 1,
   // 2) by row reads of the swizzled tiles, dO^T and Q^T (phases 3, 4) by
-  // transpose reads.
+  // transpose reads. The tiles are triple-buffered, so the next tile is
+  // complete while this one runs: the last slots read its LSE and D, the ring
+  // carries its first kA operands, and its first MFMA does not wait for LDS
+  // after the barrier.
   // The slots are generated at compile time (static_for, if constexpr), so
   // the code of each is straight-line from the start: with a run-time slot
   // index the optimiser moved MFMAs of the rolled loop several slots late.
@@ -503,12 +530,45 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   // s_nop: the compiler counts every asm statement as one wait state when it
   // spaces an MFMA and a VALU read of its result, so an empty one would
   // leave such a read a wait state short.
-  auto tile_body = [&](int t, const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld,
-                       auto mask_tag, auto&& next) __attribute__((always_inline)) {
+  constexpr int N1 = DK, N2 = DK, N3 = PK * DB, N4 = PK * DB;
+  constexpr int NM = N1 + N2 + N3 + N4;
+  constexpr int kA = bwd::kDkdvAhead;
+  static_assert(NM - kA - 2 * PK >= N1, "next-tile LSE/D reads after phase 1");
+  // operand of MFMA j of the tile in (lq, lg)
+  auto operand = [&](auto jt, const uint8_t* lq, const uint8_t* lg) __attribute__((always_inline)) -> u32x4 {
+    constexpr int j = decltype(jt)::value;
+    if constexpr (j < N1) {
+      return *reinterpret_cast<const u32x4*>(lq + roff[j]);
+    } else if constexpr (j < N1 + N2) {
+      return *reinterpret_cast<const u32x4*>(lg + roff[j - N1]);
+    } else {
+      constexpr bool dv_phase = j < N1 + N2 + N3;
+      constexpr int m = dv_phase ? j - N1 - N2 : j - N1 - N2 - N3;
+      return bwd::tr_operand((dv_phase ? lg : lq) + (m / DB) * 16 * ROWB, toff[m % DB][0],
+                             toff[m % DB][1]);
+    }
+  };
+  // LSE and D of this lane's 16 queries (element r is query
+  // qt0 + 16*(r>>3) + 8*hf + (r&7)), half i of the reads
+  u32x4 lq4[2 * PK], dq4[2 * PK], ring[kA];
+  auto read_ld = [&](auto it, const float* ll, const float* ld) __attribute__((always_inline)) {
+    constexpr int i = decltype(it)::value;
+    const int qr = 16 * (i >> 1) + 8 * hf + 4 * (i & 1);
+    lq4[i] = *reinterpret_cast<const u32x4*>(ll + qr);
+    dq4[i] = *reinterpret_cast<const u32x4*>(ld + qr);
+  };
+  // what a tile needs read before its first slot
+  auto prefetch = [&](const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld)
+                      __attribute__((always_inline)) {
+    bwd::static_for<0, 2 * PK>([&](auto it) __attribute__((always_inline)) { read_ld(it, ll, ld); });
+    bwd::static_for<0, kA>([&](auto jt) __attribute__((always_inline)) {
+      ring[decltype(jt)::value] = operand(jt, lq, lg);
+    });
+  };
+  auto tile_body = [&](int t, const uint8_t* lq, const uint8_t* lg, auto mask_tag, auto&& next,
+                       const uint8_t* nq, const uint8_t* ng, const float* nll, const float* nld)
+                       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int N1 = DK, N2 = DK, N3 = PK * DB, N4 = PK * DB;
-    constexpr int NM = N1 + N2 + N3 + N4;
-    constexpr int kA = bwd::kDkdvAhead;
     constexpr int EP1 = 16 / N1;  // -LSE log2 e values per phase-1 slot
     static_assert(EP1 % 2 == 0, "pairs per slot");
     // P over the N2 + N3/2 - 1 slots from N1 on, each half done before the
@@ -519,36 +579,10 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     static_assert(SpreadP::lo(N1 + N2) >= 8 && SpreadP::lo(N1 + N2 + N3 / 2) == 16, "P in time");
     static_assert(SpreadD::lo(N1 + N2 + N3) >= 8 && SpreadD::lo(N1 + N2 + N3 + N4 / 2) == 16,
                   "dS in time");
+    // the next tile's LSE and D are read from slot kLd on (this tile's are
+    // dead by then: phase 1 and the seeding of dP' use them)
+    constexpr int kLd = NM - kA - 2 * PK;
     const int qt0 = t * BQt;
-    // LSE and D of this lane's 16 queries (element r is query
-    // qt0 + 16*(r>>3) + 8*hf + (r&7)), read first: they feed phases 1 and 2
-    u32x4 lq4[2 * PK], dq4[2 * PK];
-#pragma unroll
-    for (int ks = 0; ks < PK; ++ks) {
-      const int qr = 16 * ks + 8 * hf;
-      lq4[2 * ks] = *reinterpret_cast<const u32x4*>(ll + qr);
-      lq4[2 * ks + 1] = *reinterpret_cast<const u32x4*>(ll + qr + 4);
-      dq4[2 * ks] = *reinterpret_cast<const u32x4*>(ld + qr);
-      dq4[2 * ks + 1] = *reinterpret_cast<const u32x4*>(ld + qr + 4);
-    }
-    auto operand = [&](auto jt) __attribute__((always_inline)) -> u32x4 {
-      constexpr int j = decltype(jt)::value;
-      if constexpr (j < N1) {
-        return *reinterpret_cast<const u32x4*>(lq + roff[j]);
-      } else if constexpr (j < N1 + N2) {
-        return *reinterpret_cast<const u32x4*>(lg + roff[j - N1]);
-      } else {
-        constexpr bool dv_phase = j < N1 + N2 + N3;
-        constexpr int m = dv_phase ? j - N1 - N2 : j - N1 - N2 - N3;
-        return bwd::tr_operand((dv_phase ? lg : lq) + (m / DB) * 16 * ROWB, toff[m % DB][0],
-                               toff[m % DB][1]);
-      }
-    };
-    u32x4 ring[kA];
-    bwd::static_for<0, kA>([&](auto jt) __attribute__((always_inline)) {
-      ring[decltype(jt)::value] = operand(jt);
-    });
-    __builtin_amdgcn_sched_barrier(0);
 
     f32x16 s, dp;
 #pragma unroll
@@ -564,10 +598,13 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     bwd::static_for<0, NM>([&](auto jt) __attribute__((always_inline)) {
       constexpr int j = decltype(jt)::value;
       const u32x4 a = ring[j % kA];
-      if constexpr (j + kA < NM) ring[j % kA] = operand(std::integral_constant<int, j + kA>{});
+      if constexpr (j + kA < NM) ring[j % kA] = operand(std::integral_constant<int, j + kA>{}, lq, lg);
+      else ring[j % kA] = operand(std::integral_constant<int, j + kA - NM>{}, nq, ng);
+      if constexpr (j >= kLd && j < kLd + 2 * PK)
+        read_ld(std::integral_constant<int, j - kLd>{}, nll, nld);
       if constexpr (j < N1) {
         s = O_::mfma(a, kf[j], s);
-        if constexpr (j == 0) next();  // the next tile's copies, once this tile's reads are out
+        if constexpr (j == 0) next();  // the tile after next: copies into the free buffer
       } else if constexpr (j < N1 + N2) {
         dp = O_::mfma(a, vf[j - N1], dp);
       } else if constexpr (j < N1 + N2 + N3) {
@@ -624,53 +661,75 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     });
   };
   // Steps: one per query tile u = 0 .. n_t-1 (tile t_begin + u), each with
-  // one barrier; tile u lives in buffer u & 1. A causal wave has nothing to
-  // do for its first `f` tiles (all their queries precede its keys); tile f
-  // is its diagonal tile (the only one that needs an element mask, as
-  // BQt = 32 keys per wave); the rest are fully visible. Rows past Nq need
-  // no mask: their Q, dO, LSE and D are zero-filled, so P = 1 and dS = 0
-  // multiply zero rows. Each kind of step is a straight-line body with the
-  // buffer parity fixed at compile time, so the accumulators stay in place.
+  // one barrier; tile u lives in buffer u % 3. At the barrier of step u the
+  // copies of tile u + 1 (issued in step u - 1) are complete and every wave
+  // is done with tile u - 1, whose buffer then takes tile u + 2. A causal
+  // wave has nothing to do for its first `f` tiles (all their queries
+  // precede its keys); tile f is its diagonal tile (the only one that needs
+  // an element mask, as BQt = 32 keys per wave); the rest are fully
+  // visible. Rows past Nq need no mask: their Q, dO, LSE and D are
+  // zero-filled, so P = 1 and dS = 0 multiply zero rows. Each kind of step
+  // is a straight-line body with the buffer index fixed at compile time, so
+  // the accumulators stay in place. The last step reads a stale buffer as
+  // its next tile (in bounds, never used).
   const int n_t = n_qtiles_all - t_begin;
   int f = CAUSAL ? min(n_t, wave) : 0;
   if (kw0 >= p.Nk) f = n_t;  // no real keys in this wave
   auto step = [&](int u, auto par, auto mode) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
+    constexpr int P1 = (P + 1) % 3, P2 = (P + 2) % 3;
     constexpr int MODE = decltype(mode)::value;  // 0 idle, 1 masked, 2 unmasked
     const int t = t_begin + u;
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    // vmcnt(0): this wave's copies of tile u + 1 are done. lgkmcnt(kA): all
+    // but its last kA LDS reads are done; those are the ring reads of tile
+    // u + 1 (LDS reads complete in order), and what the barrier frees is
+    // tile u - 1's buffer
+    static_assert(kA < 16, "lgkmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (kA << 8));
     sync::bare_barrier();
+    using I = std::integral_constant<int, P>;
+    using I1 = std::integral_constant<int, P1>;
+    using I2 = std::integral_constant<int, P2>;
     auto next = [&]() __attribute__((always_inline)) {
-      if (u + 1 < n_t) {
-        if constexpr (P == 0) issue(t + 1, lds_q1, lds_g1, lds_l1, lds_d1);
-        else issue(t + 1, lds_q0, lds_g0, lds_l0, lds_d0);
-      }
+      if (u + 2 < n_t) issue(t + 2, bq(I2{}), bg(I2{}), bl(I2{}), bd(I2{}));
     };
     if constexpr (MODE != 0) {
       using M = std::integral_constant<bool, MODE == 1>;
-      if constexpr (P == 0) tile_body(t, lds_q0, lds_g0, lds_l0, lds_d0, M{}, next);
-      else tile_body(t, lds_q1, lds_g1, lds_l1, lds_d1, M{}, next);
+      tile_body(t, bq(I{}), bg(I{}), M{}, next, bq(I1{}), bg(I1{}), bl(I1{}), bd(I1{}));
     } else {
       next();
+      prefetch(bq(I1{}), bg(I1{}), bl(I1{}), bd(I1{}));
     }
   };
-  using Even = std::integral_constant<int, 0>;
-  using Odd = std::integral_constant<int, 1>;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   auto run = [&](int u0, int u1, auto mode) __attribute__((always_inline)) {
     int u = u0;
-    if (u < u1 && (u & 1)) step(u++, Odd{}, mode);
-    for (; u + 1 < u1; u += 2) {
-      step(u, Even{}, mode);
-      step(u + 1, Odd{}, mode);
+    if (u < u1 && u % 3 == 1) step(u++, B1{}, mode);
+    if (u < u1 && u % 3 == 2) step(u++, B2{}, mode);
+    for (; u + 2 < u1; u += 3) {
+      step(u, B0{}, mode);
+      step(u + 1, B1{}, mode);
+      step(u + 2, B2{}, mode);
     }
-    if (u < u1) step(u, Even{}, mode);
+    if (u < u1) step(u++, B0{}, mode);
+    if (u < u1) step(u, B1{}, mode);
   };
+  // prologue: tile 0 complete and visible, tile 1 in flight, tile 0's
+  // first reads issued
   if (n_t > 0) issue(t_begin, lds_q0, lds_g0, lds_l0, lds_d0);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+  if (n_t > 1) issue(t_begin + 1, lds_q1, lds_g1, lds_l1, lds_d1);
+  sync::bare_barrier();
+  prefetch(lds_q0, lds_g0, lds_l0, lds_d0);
   run(0, f, std::integral_constant<int, 0>{});
   if constexpr (CAUSAL) {
     if (f < n_t) {
-      if (f & 1) step(f, Odd{}, std::integral_constant<int, 1>{});
-      else step(f, Even{}, std::integral_constant<int, 1>{});
+      const int fb = f % 3;
+      if (fb == 0) step(f, B0{}, std::integral_constant<int, 1>{});
+      else if (fb == 1) step(f, B1{}, std::integral_constant<int, 1>{});
+      else step(f, B2{}, std::integral_constant<int, 1>{});
     }
   }
   run(f + (CAUSAL ? 1 : 0), n_t, std::integral_constant<int, 2>{});
@@ -685,7 +744,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     const uint32_t range = (uint32_t)(nrows - 1) * row_bytes + 2 * D;
     const auto out_k = make_rsrc(p.dk + kvo + (size_t)k0 * rs, range);
     const auto out_v = make_rsrc(p.dv + kvo + (size_t)k0 * rs, range);
-    uint8_t* const slot = wave == 0 ? lds_q0 : wave == 1 ? lds_q1 : wave == 2 ? lds_g0 : lds_g1;
+    uint8_t* const slot = wave == 0 ? lds_q0 : wave == 1 ? lds_q1 : wave == 2 ? lds_q2 : lds_g0;
     const uint32_t gbase = (uint32_t)(wave * 32) * row_bytes;
     store_rows<O_, D>(dkt, -p.scale, slot, out_k, gbase, row_bytes, lane);  // dkt holds -dK^T
     store_rows<O_, D>(dvt, 1.f, slot, out_v, gbase, row_bytes, lane);
