@@ -59,6 +59,7 @@ namespace bwd {
 // workgroup), kBK (keys per dq tile) and kBQt (queries per dkdv tile) are in
 // mha_tiles.hpp
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kDkdvAhead = 4;  // dK/dV operand reads issued this many MFMAs ahead
 
 using mha::lds_read_tr16;
 using mha::t_swz;

@@ -36,7 +36,6 @@ constexpr int kBQ = 32 * kWaves;   // query rows per dq workgroup
 constexpr int kBKV = 32 * kWaves;  // keys per dkdv workgroup
 constexpr int kBK = 64;            // keys per tile streamed by dq
 constexpr int kBQt = 32;           // queries per tile streamed by dkdv
-constexpr int kDkdvAhead = 4;      // dkdv operand reads issued this many MFMAs ahead
 }  // namespace bwd
 
 namespace proj {  // output projection GEMM
