@@ -48,6 +48,14 @@ namespace kl {
 // kWaves, kThreads, kBQ (query rows per workgroup) and kBK (keys per tile)
 // are in mha_tiles.hpp
 constexpr float kLn2 = 0.69314718055994531f;
+// Maximum over the two halves of the wave (lanes l and l ^ 32), as a
+// three-input maximum from -inf
+__device__ __forceinline__ float max_halves3(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return fmaxf(fmaxf(-__builtin_inff(), __builtin_bit_cast(float, lo)), __builtin_bit_cast(float, hi));
+}
 }  // namespace kl
 
 template <typename T, int D, bool CAUSAL>
@@ -200,14 +208,16 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
           x2[r] = vis ? x2[r] : NEG_INF;
         }
       }
-      float t1 = x1[0], t2 = x2[0];
+      // chains started from -inf: the compiler then forms three-input
+      // maxima throughout, with no NaN-quieting copies of the raw scores
+      float t1 = NEG_INF, t2 = NEG_INF;
 #pragma unroll
-      for (int r = 1; r < 16; ++r) {
+      for (int r = 0; r < 16; ++r) {
         t1 = fmaxf(t1, x1[r]);
         t2 = fmaxf(t2, x2[r]);
       }
-      t1 = max_halves(t1);
-      t2 = max_halves(t2);
+      t1 = kl::max_halves3(t1);
+      t2 = kl::max_halves3(t2);
       // A row that sees no key of this block (causal, diagonal tile) has
       // t = -inf and never moves its maximum here; while a row has seen no
       // key at all its m * c stays 0, so masked weights are exp2(-inf) = 0.
