@@ -159,6 +159,11 @@ SHAPES = [
     (1, 8, 300, 300, 128, "bf16", True),   # B*H = 8: XCD-grouped order
     (2, 8, 200, 333, 64, "fp16", False),
     (1, 16, 257, 257, 128, "bf16", True),
+    # the dK/dV kernel's three query-tile buffers: 2, 3 and 5 tiles of 32
+    # queries per key block (runs shorter than, equal to and past one turn)
+    (2, 1, 64, 64, 128, "fp16", True),
+    (1, 2, 96, 96, 128, "bf16", True),     # wave 3's keys all past Nk
+    (1, 1, 160, 160, 128, "bf16", False),
 ]
 
 
