@@ -12,6 +12,12 @@ regime of the FlashAttention long-sequence post). Prints ONE JSON line.
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                   [--pass fwd|bwd|splitkv|kl|proj] [--no-cpu-baseline]
                   [--cpu-seconds S] [--calib-copy-mib M] [--counters]
+                  [--no-gemm-ref]
+
+For the MFMA-bound passes the roofline object also carries the rate of the
+vendor library's bf16 GEMM (torch.matmul, 8192^3) timed the same way on the
+same box after the kernel: the dense rate the engine clock sustains under a
+pure GEMM load, beside the published peak (frac_of_vendor_gemm).
 
 With --counters, rocprofv3 counter passes over this script run first (as
 child processes, before this process touches the GPU) and their HBM bytes,
@@ -389,6 +395,32 @@ def settle(torch, step, min_s: float = SETTLE_S) -> int:
     return n
 
 
+VENDOR_GEMM_N = 8192
+
+
+def vendor_gemm_ref(torch) -> dict:
+    """The vendor library's bf16 GEMM (torch.matmul, N x N x N, N = 8192) on
+    this box, warmed up, settled and timed back to back like the kernels: the
+    dense MFMA rate the engine clock sustains under a pure GEMM load, beside
+    the published peak. Runs after the kernel's timed region; not part of
+    any step."""
+    n = VENDOR_GEMM_N
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+
+    def step():
+        torch.matmul(a, b)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    settle(torch, step)
+    ms, _ = time_steps(torch, torch.cuda.current_stream(), step, 20)
+    del a, b
+    return {"what": f"torch.matmul bf16 {n}x{n}x{n} (vendor GEMM library), same box",
+            "ms": round(ms, 4), "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+
+
 def apply_live(roof: dict, live, flops: float, ms_per_step: float, dev: dict) -> None:
     """Put live counter results (--counters) into the roofline object, in
     place of the committed summaries' figures."""
@@ -504,6 +536,10 @@ def bench_proj(args, torch, mha, w, live=None) -> int:
         "kernel_source_sha256_16": kernel_source_hash(KERNEL_SOURCES_PROJ),
         "device": device_info(torch),
     }
+    if not args.no_gemm_ref:
+        ref = vendor_gemm_ref(torch)
+        line["roofline"]["vendor_bf16_gemm"] = ref
+        line["roofline"]["frac_of_vendor_gemm"] = round(achieved / ref["tflops"], 4)
     apply_live(line["roofline"], live, w.flops, ms, line["device"])
     if not args.no_cpu_baseline:
         print("bench.py: timing the fp64 oracle on the host (cpu_baseline) ...", file=sys.stderr,
@@ -566,7 +602,7 @@ def _pmc_run(rocprof, counters, which, workload, steps, calib, workdir, timeout_
     line, dispatches in order as dicts of kernel key and counter values)."""
     out = tempfile.mkdtemp(prefix="pmc_", dir=workdir)
     child = [sys.executable, os.path.abspath(__file__), "--pass", which, "--workload", workload,
-             "--steps", str(steps), "--warmup", "1", "--no-cpu-baseline"]
+             "--steps", str(steps), "--warmup", "1", "--no-cpu-baseline", "--no-gemm-ref"]
     if calib:
         child += ["--calib-copy-mib", str(CALIB_MIB)]
     cmd = [rocprof, "--pmc", *counters, "--output-format", "csv", "-d", out, "-o", "p", "--", *child]
@@ -672,6 +708,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-gemm-ref", action="store_true",
+                    help="skip the vendor bf16 GEMM reference rate (MFMA-bound passes)")
     ap.add_argument("--counters", action="store_true",
                     help="also run rocprofv3 counter passes (HBM bytes, MFMA busy, engine "
                          "clock) over this script first and report them live")
@@ -862,6 +900,10 @@ def main() -> int:
             roof["peak_at_sclk_under_load"] = round(pk, 1)
             roof["frac_at_sclk_under_load"] = round(achieved / pk, 4)
     roof["launch_ms"] = launch_fields(ms_per_step, per)
+    if roof["bound"] == "mfma" and not args.no_gemm_ref:
+        ref = vendor_gemm_ref(torch)
+        roof["vendor_bf16_gemm"] = ref
+        roof["frac_of_vendor_gemm"] = round(achieved / ref["tflops"], 4)
     if flushed_ms is not None:
         roof["mall_flushed"] = {"flush_mib": MALL_FLUSH_MIB, "launch_ms_median": round(flushed_ms, 5),
                                 "tflops": round(flops / (flushed_ms * 1e-3) / 1e12, 2),
