@@ -24,8 +24,14 @@ mha_status_t launch_bwd(const mha::BwdParams& pd, const mha::BwdParams& pq,
   }
   if (e == hipSuccess && run_k) {
     void* a2[] = {const_cast<mha::BwdParams*>(&pk)};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&mha::mha_bwd_dkdv_kernel<T, D, C>),
-                        dim3(pk.n_blocks), dim3(mha::bwd::kThreads), a2, 0, stream);
+    if constexpr (D == 128) {
+      // producer/consumer wave pairs: two waves per SIMD
+      e = hipLaunchKernel(reinterpret_cast<const void*>(&mha::mha_bwd_dkdv_pair_kernel<T, D, C>),
+                          dim3(pk.n_blocks), dim3(2 * mha::bwd::kThreads), a2, 0, stream);
+    } else {
+      e = hipLaunchKernel(reinterpret_cast<const void*>(&mha::mha_bwd_dkdv_kernel<T, D, C>),
+                          dim3(pk.n_blocks), dim3(mha::bwd::kThreads), a2, 0, stream);
+    }
   }
   if (e != hipSuccess) {
     (void)hipGetLastError();

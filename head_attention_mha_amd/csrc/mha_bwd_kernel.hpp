@@ -752,4 +752,437 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
   }
 }
 
+// ---- dK, dV at d = 128: producer/consumer wave pairs -----------------------
+// The kernel above runs one wave per SIMD at d = 128 (~330 registers), and a
+// lone wave draws only ~1 KiB per 29 cycles from LDS with 16-byte reads: its
+// tile is bound by its own LDS reads, not by the MFMA pipe. Here each SIMD
+// runs two waves of one workgroup on the same 32 keys:
+// * a producer (waves 0-3) holds the K and -V fragments and, for query tile
+//   u, computes S = Q K^T and dP' = D - dO V^T (16 MFMAs) with -LSE log2 e,
+//   P and -dS = P o dP' between and after them, and hands P and -dS (packed,
+//   the MFMA B-operand fragments, 4 KiB per wave) to its consumer through
+//   LDS;
+// * the consumer (waves 4-7, on the same SIMD, same keys) holds dV^T and
+//   -dK^T and, in the same step, accumulates dV^T += dO^T P and
+//   -dK^T += Q^T (-dS) for tile u - 1 (16 MFMAs, the transpose reads).
+// Each wave holds about half of the state, so both fit 256 registers, and
+// each issues about half of a tile's LDS reads; the MFMA pipe of the SIMD
+// takes both waves' MFMAs. One barrier per step orders the hand-over (step
+// u's producers write exchange buffer u % 2, step u + 1's consumers read
+// it). Q/dO tiles rotate through four buffers (tile u - 1 is still read by
+// the consumers while tile u + 2 is copied in); the consumers issue the
+// copies. The arithmetic and its order per element are those of the kernel
+// above, so the results are identical to it.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(2 * bwd::kThreads) void mha_bwd_dkdv_pair_kernel(BwdParams p) {
+  using O_ = Ops<T>;
+  constexpr int BQt = bwd::kBQt;
+  constexpr int kBKV = bwd::kBKV;
+  constexpr int NP = bwd::kWaves;          // wave pairs, 32 keys each
+  constexpr int DK = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int PK = BQt / 16;
+  constexpr int CH = D / 8;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BQt * ROWB;        // Q or dO tile
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int NCPW = TILEB / 1024 / NP;  // copies per consumer wave per tensor
+  constexpr int XB = 2 * PK * 1024;        // exchange bytes per pair: P and -dS, 16 B per lane each
+  static_assert(NCPW >= 1 && (NP * RPI) % 16 == 0, "copy layout");
+  constexpr int kA = bwd::kDkdvAhead;
+  constexpr int NMP = 2 * DK;              // producer MFMAs per tile
+  constexpr int NMC = 2 * PK * DB;         // consumer MFMAs per tile
+
+  // Four buffers of each tile kind, two exchange buffers; separate objects,
+  // so that the compiler sees that a copy into one buffer does not write
+  // another and inserts no wait for the copies before other LDS reads.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_q0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_q1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_q2[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_q3[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_g0[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_g1[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_g2[TILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_g3[TILEB];
+  // LSE (copied by pair 0's consumer) and D (pair 1's) of the tile's
+  // queries: one 256-byte copy each, of which the first 128 bytes are the 32
+  // values
+  __shared__ __attribute__((aligned(256))) float lds_l0[64];
+  __shared__ __attribute__((aligned(256))) float lds_l1[64];
+  __shared__ __attribute__((aligned(256))) float lds_l2[64];
+  __shared__ __attribute__((aligned(256))) float lds_l3[64];
+  __shared__ __attribute__((aligned(256))) float lds_d0[64];
+  __shared__ __attribute__((aligned(256))) float lds_d1[64];
+  __shared__ __attribute__((aligned(256))) float lds_d2[64];
+  __shared__ __attribute__((aligned(256))) float lds_d3[64];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_x0[NP * XB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_x1[NP * XB];
+  // buffer i (compile-time) of each kind
+  auto bq = [&](auto it) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int i = decltype(it)::value & 3;
+    return i == 0 ? lds_q0 : i == 1 ? lds_q1 : i == 2 ? lds_q2 : lds_q3;
+  };
+  auto bg = [&](auto it) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int i = decltype(it)::value & 3;
+    return i == 0 ? lds_g0 : i == 1 ? lds_g1 : i == 2 ? lds_g2 : lds_g3;
+  };
+  auto bl = [&](auto it) __attribute__((always_inline)) -> float* {
+    constexpr int i = decltype(it)::value & 3;
+    return i == 0 ? lds_l0 : i == 1 ? lds_l1 : i == 2 ? lds_l2 : lds_l3;
+  };
+  auto bd = [&](auto it) __attribute__((always_inline)) -> float* {
+    constexpr int i = decltype(it)::value & 3;
+    return i == 0 ? lds_d0 : i == 1 ? lds_d1 : i == 2 ? lds_d2 : lds_d3;
+  };
+  auto bx = [&](auto it) __attribute__((always_inline)) -> uint8_t* {
+    return (decltype(it)::value & 1) == 0 ? lds_x0 : lds_x1;
+  };
+
+  // work item: (batch, head, key block), a head's blocks on one XCD, one
+  // workgroup per CU
+  const int lin = blockIdx.x;
+  const int BH = p.B * p.H;
+  const bool by_xcd = (BH & 7) == 0;
+  const int nh = by_xcd ? BH >> 3 : BH;
+  const int kk = by_xcd ? engine_order(lin >> 3, nh * p.n_tiles, 32) : lin;
+  const int ki = kk / nh;
+  const int hh = kk - ki * nh;
+  const int bh = by_xcd ? 8 * hh + (lin & 7) : hh;
+  const int kt = ki;
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int k0 = kt * kBKV;
+
+  const size_t rs = (size_t)p.H * D;
+  const size_t qo = ((size_t)b * p.Nq * p.H + h) * D;
+  const size_t kvo = ((size_t)b * p.Nk * p.H + h) * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & (NP - 1);
+  const bool consumer = wave >= NP;
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hf = lane >> 5;
+  const int kw0 = k0 + pair * 32;
+  const int my_k = kw0 + ln;
+
+  // query tiles: causal blocks start at the first query that sees key k0
+  const int n_qtiles_all = (p.Nq + BQt - 1) / BQt;
+  const int t_begin = CAUSAL ? min(k0 / BQt, n_qtiles_all) : 0;
+  const int n_t = n_qtiles_all - t_begin;
+  // a causal pair has nothing to do for its first f tiles; tile f is its
+  // diagonal tile (element mask), the rest are fully visible (rows past Nq:
+  // zero-filled Q, dO, LSE and D, so P = 1 and dS = 0 on zero rows)
+  int f = CAUSAL ? min(n_t, pair) : 0;
+  if (kw0 >= p.Nk) f = n_t;  // no real keys in this pair
+
+  uint32_t roff[DK];
+  {
+    const int row = k_row_order(ln);
+    const int sw = bwd::t_swz<D>(row);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) roff[i] = row * ROWB + 16 * ((2 * i + hf) ^ sw);
+  }
+  uint32_t toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) toff[db][r] = bwd::tr_off<D>(lane, db, r);
+  // this lane's 16 bytes of a pair's exchange block
+  const uint32_t xoff = (uint32_t)(pair * XB + 16 * lane);
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  // steps u0 .. u1-1 of one kind, tile buffers u % 4 fixed at compile time
+  auto run4 = [&](int u0, int u1, auto&& step) __attribute__((always_inline)) {
+    int u = u0;
+    if (u < u1 && (u & 3) == 1) step(u++, B1{});
+    if (u < u1 && (u & 3) == 2) step(u++, B2{});
+    if (u < u1 && (u & 3) == 3) step(u++, B3{});
+    for (; u + 3 < u1; u += 4) {
+      step(u, B0{});
+      step(u + 1, B1{});
+      step(u + 2, B2{});
+      step(u + 3, B3{});
+    }
+    if (u < u1) step(u++, B0{});
+    if (u < u1) step(u++, B1{});
+    if (u < u1) step(u, B2{});
+  };
+  auto at4 = [&](int u, auto&& step) __attribute__((always_inline)) {
+    switch (u & 3) {
+      case 0: step(u, B0{}); break;
+      case 1: step(u, B1{}); break;
+      case 2: step(u, B2{}); break;
+      default: step(u, B3{}); break;
+    }
+  };
+
+  // copies per consumer wave per tile: NCPW each of Q and dO, plus LSE on
+  // pair 0 and D on pair 1 (their rows of this (b, h), chosen once)
+  uint32_t c_off[NCPW];
+#pragma unroll
+  for (int c = 0; c < NCPW; ++c) {
+    const int row = (c * NP + pair) * RPI + lane / CH;
+    c_off[c] = row * row_bytes + 16 * ((lane % CH) ^ bwd::t_swz<D>(row));
+  }
+  const float* const lsd_src = (pair == 0 ? p.lse : p.delta) + (size_t)bh * p.Nq;
+  auto issue = [&](int t, uint8_t* lq, uint8_t* lg, float* ll, float* ld) __attribute__((always_inline)) {
+    const int nvalid = min(BQt, p.Nq - t * BQt);
+    const uint32_t bytes = (uint32_t)(nvalid - 1) * row_bytes + ROWB;
+    const auto rq = make_rsrc(p.q + qo + (size_t)t * BQt * rs, bytes);
+    const auto rg = make_rsrc(p.dout + qo + (size_t)t * BQt * rs, bytes);
+#pragma unroll
+    for (int c = 0; c < NCPW; ++c) dma16(rq, lq + (c * NP + pair) * 1024, c_off[c]);
+#pragma unroll
+    for (int c = 0; c < NCPW; ++c) dma16(rg, lg + (c * NP + pair) * 1024, c_off[c]);
+    if (pair < 2) {
+      const auto rl = make_rsrc(lsd_src + t * BQt, (uint32_t)nvalid * 4);
+      bwd::dma4(rl, reinterpret_cast<uint8_t*>(pair == 0 ? ll : ld), 4 * lane);
+    }
+  };
+
+  const float c = p.scale_log2;
+
+  if (!consumer) {
+    // ---------------------------------------------------------- producer
+    // K and -V fragments of this pair's keys (B operands), read once
+    u32x4 kf[DK], vf[DK];
+    if (my_k < p.Nk) {
+      const uint16_t* krow = p.k + kvo + (size_t)my_k * rs + 8 * hf;
+      const uint16_t* vrow = p.v + kvo + (size_t)my_k * rs + 8 * hf;
+#pragma unroll
+      for (int i = 0; i < DK; ++i) {
+        kf[i] = *reinterpret_cast<const u32x4*>(krow + 16 * i);
+        vf[i] = *reinterpret_cast<const u32x4*>(vrow + 16 * i);
+        // negated (sign bits flipped, exact): the dP MFMAs then compute D - dP
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vf[i][w] ^= 0x80008000u;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DK; ++i) kf[i] = vf[i] = u32x4{0, 0, 0, 0};
+    }
+    // operand of MFMA j (row reads: Q rows for S, dO rows for dP)
+    auto operand = [&](auto jt, const uint8_t* lq, const uint8_t* lg) __attribute__((always_inline)) -> u32x4 {
+      constexpr int j = decltype(jt)::value;
+      if constexpr (j < DK) return *reinterpret_cast<const u32x4*>(lq + roff[j]);
+      else return *reinterpret_cast<const u32x4*>(lg + roff[j - DK]);
+    };
+    // LSE and D of this lane's 16 queries (element r is query
+    // t*BQt + 16*(r>>3) + 8*hf + (r&7)), half i of the reads
+    u32x4 lq4[2 * PK], dq4[2 * PK], ring[kA];
+    auto read_ld = [&](auto it, const float* ll, const float* ld) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;
+      const int qr = 16 * (i >> 1) + 8 * hf + 4 * (i & 1);
+      lq4[i] = *reinterpret_cast<const u32x4*>(ll + qr);
+      dq4[i] = *reinterpret_cast<const u32x4*>(ld + qr);
+    };
+    // what a tile needs read before its first slot
+    auto prefetch = [&](const uint8_t* lq, const uint8_t* lg, const float* ll, const float* ld)
+                        __attribute__((always_inline)) {
+      bwd::static_for<0, 2 * PK>([&](auto it) __attribute__((always_inline)) { read_ld(it, ll, ld); });
+      bwd::static_for<0, kA>([&](auto jt) __attribute__((always_inline)) {
+        ring[decltype(jt)::value] = operand(jt, lq, lg);
+      });
+    };
+    // One query tile: 2*DK fenced slots (S, then dP'), each with one MFMA,
+    // the operand read kA MFMAs ahead (on into the next tile) and a share of
+    // the VALU work: -LSE log2 e in the S slots, P in the dP' slots; -dS after
+    // them; then P and -dS to the exchange block. The next tile's LSE and D
+    // are read from slot kLd on (this tile's are used by then).
+    constexpr int kLd = NMP - kA - 2 * PK;
+    static_assert(kLd >= DK, "next-tile LSE/D reads after the S slots");
+    constexpr int EP = 16 / DK;  // elements per slot (-LSE log2 e, P)
+    static_assert(EP % 2 == 0, "pairs per slot");
+    auto tile = [&](int t, const uint8_t* lq, const uint8_t* lg, auto mask_tag, const uint8_t* nq,
+                    const uint8_t* ng, const float* nll, const float* nld, uint8_t* xb)
+                    __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int qt0 = t * BQt;
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // (read as plain integers first: __builtin_bit_cast of a vector
+        // element reads element 0)
+        const uint32_t bb = dq4[r >> 2][r & 3];
+        s[r] = 0.f;
+        dp[r] = __builtin_bit_cast(float, bb);
+      }
+      float nl[16], pr[16];
+      u32x4 pp[PK], dsp[PK];
+      bwd::static_for<0, NMP>([&](auto jt) __attribute__((always_inline)) {
+        constexpr int j = decltype(jt)::value;
+        const u32x4 a = ring[j % kA];
+        if constexpr (j + kA < NMP) ring[j % kA] = operand(std::integral_constant<int, j + kA>{}, lq, lg);
+        else ring[j % kA] = operand(std::integral_constant<int, j + kA - NMP>{}, nq, ng);
+        if constexpr (j >= kLd && j < kLd + 2 * PK)
+          read_ld(std::integral_constant<int, j - kLd>{}, nll, nld);
+        if constexpr (j < DK) {
+          s = O_::mfma(a, kf[j], s);
+          bwd::static_for<0, EP / 2>([&](auto it) __attribute__((always_inline)) {
+            constexpr int r = j * EP + 2 * decltype(it)::value;
+            const uint32_t b0 = lq4[r >> 2][r & 3], b1 = lq4[(r + 1) >> 2][(r + 1) & 3];
+            float x0 = __builtin_bit_cast(float, b0) * -bwd::kLog2e;
+            float x1 = __builtin_bit_cast(float, b1) * -bwd::kLog2e;
+            asm volatile("s_nop 0" : "+v"(x0), "+v"(x1));
+            nl[r] = x0;
+            nl[r + 1] = x1;
+          });
+        } else {
+          dp = O_::mfma(a, vf[j - DK], dp);
+          bwd::static_for<0, EP / 2>([&](auto it) __attribute__((always_inline)) {
+            constexpr int r = (j - DK) * EP + 2 * decltype(it)::value;
+            float x[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              x[e] = fast_exp2(__builtin_fmaf(s[r + e], c, nl[r + e]));
+              if constexpr (MASK) {
+                const int q = qt0 + 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
+                const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
+                x[e] = vis ? x[e] : 0.f;
+              }
+              pr[r + e] = x[e];
+            }
+            uint32_t w = O_::pack(x[0], x[1]);
+            asm volatile("s_nop 0" : "+v"(w));
+            pp[r >> 3][(r & 7) >> 1] = w;
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // -dS = P o dP' (dP' = D - dP), packed
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        dsp[r >> 3][(r & 7) >> 1] = O_::pack(pr[r] * dp[r], pr[r + 1] * dp[r + 1]);
+#pragma unroll
+      for (int ks = 0; ks < PK; ++ks) {
+        *reinterpret_cast<u32x4*>(xb + xoff + ks * 1024) = pp[ks];
+        *reinterpret_cast<u32x4*>(xb + xoff + (PK + ks) * 1024) = dsp[ks];
+      }
+    };
+    // step u: tile u, exchange buffer u % 2
+    auto step_of = [&](auto mode) __attribute__((always_inline)) {
+      return [&, mode](int u, auto par) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        constexpr int MODE = decltype(mode)::value;  // 0 idle, 1 masked, 2 unmasked
+        using I = std::integral_constant<int, P>;
+        using I1 = std::integral_constant<int, P + 1>;
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0): exchange writes done
+        sync::bare_barrier();
+        if constexpr (MODE != 0) {
+          using M = std::integral_constant<bool, MODE == 1>;
+          tile(t_begin + u, bq(I{}), bg(I{}), M{}, bq(I1{}), bg(I1{}), bl(I1{}), bd(I1{}), bx(I{}));
+        } else {
+          prefetch(bq(I1{}), bg(I1{}), bl(I1{}), bd(I1{}));
+        }
+      };
+    };
+    // prologue (the consumers copy tiles 0 and 1): tile 0's first reads
+    sync::bare_barrier();
+    prefetch(lds_q0, lds_g0, lds_l0, lds_d0);
+    run4(0, f, step_of(std::integral_constant<int, 0>{}));
+    if constexpr (CAUSAL) {
+      if (f < n_t) at4(f, step_of(std::integral_constant<int, 1>{}));
+    }
+    run4(f + (CAUSAL ? 1 : 0), n_t, step_of(std::integral_constant<int, 2>{}));
+    // the consumers' last step (tile n_t - 1)
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    sync::bare_barrier();
+    // epilogue: the consumers store
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    sync::bare_barrier();
+  } else {
+    // ---------------------------------------------------------- consumer
+    f32x16 dkt[DB], dvt[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
+    // operand of MFMA j: dO^T (dV phase) or Q^T (dK phase) by transpose reads
+    auto operand = [&](auto jt, const uint8_t* lq, const uint8_t* lg) __attribute__((always_inline)) -> u32x4 {
+      constexpr int j = decltype(jt)::value;
+      constexpr bool dv_phase = j < PK * DB;
+      constexpr int m = dv_phase ? j : j - PK * DB;
+      return bwd::tr_operand((dv_phase ? lg : lq) + (m / DB) * 16 * ROWB, toff[m % DB][0],
+                             toff[m % DB][1]);
+    };
+    u32x4 ring[kA];
+    auto prefetch = [&](const uint8_t* lq, const uint8_t* lg) __attribute__((always_inline)) {
+      bwd::static_for<0, kA>([&](auto jt) __attribute__((always_inline)) {
+        ring[decltype(jt)::value] = operand(jt, lq, lg);
+      });
+    };
+    // tile u - 1: P and -dS from the exchange block, then 2*PK*DB fenced
+    // slots (dV^T, then -dK^T), the operand read kA MFMAs ahead (on into
+    // tile u)
+    auto tile = [&](const uint8_t* lq, const uint8_t* lg, const uint8_t* xb, const uint8_t* nq,
+                    const uint8_t* ng) __attribute__((always_inline)) {
+      u32x4 pp[PK], dsp[PK];
+#pragma unroll
+      for (int ks = 0; ks < PK; ++ks) {
+        pp[ks] = *reinterpret_cast<const u32x4*>(xb + xoff + ks * 1024);
+        dsp[ks] = *reinterpret_cast<const u32x4*>(xb + xoff + (PK + ks) * 1024);
+      }
+      bwd::static_for<0, NMC>([&](auto jt) __attribute__((always_inline)) {
+        constexpr int j = decltype(jt)::value;
+        const u32x4 a = ring[j % kA];
+        if constexpr (j + kA < NMC) ring[j % kA] = operand(std::integral_constant<int, j + kA>{}, lq, lg);
+        else ring[j % kA] = operand(std::integral_constant<int, j + kA - NMC>{}, nq, ng);
+        if constexpr (j < PK * DB) {
+          dvt[j % DB] = O_::mfma(a, pp[j / DB], dvt[j % DB]);
+        } else {
+          constexpr int m = j - PK * DB;
+          dkt[m % DB] = O_::mfma(a, dsp[m / DB], dkt[m % DB]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // step u: copies of tile u + 2, then tile u - 1 (its Q/dO in buffer
+    // (u - 1) % 4, its exchange block in buffer (u - 1) % 2)
+    auto step_of = [&](auto active) __attribute__((always_inline)) {
+      return [&, active](int u, auto par) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        using I = std::integral_constant<int, P>;
+        using Im1 = std::integral_constant<int, P + 3>;
+        using I2 = std::integral_constant<int, P + 2>;
+        // vmcnt(0): this wave's copies of tile u + 1 are done. lgkmcnt(kA):
+        // all but its last kA LDS reads are done; those are the ring reads of
+        // tile u (LDS reads complete in order)
+        static_assert(kA < 16, "lgkmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0070 | (kA << 8));
+        sync::bare_barrier();
+        if (u + 2 < n_t) issue(t_begin + u + 2, bq(I2{}), bg(I2{}), bl(I2{}), bd(I2{}));
+        if constexpr (decltype(active)::value) tile(bq(Im1{}), bg(Im1{}), bx(Im1{}), bq(I{}), bg(I{}));
+        else prefetch(bq(I{}), bg(I{}));
+      };
+    };
+    // prologue: tile 0 complete and visible, tile 1 in flight
+    if (n_t > 0) issue(t_begin, lds_q0, lds_g0, lds_l0, lds_d0);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    if (n_t > 1) issue(t_begin + 1, lds_q1, lds_g1, lds_l1, lds_d1);
+    sync::bare_barrier();
+    // step u works on tile u - 1: idle for u <= f (no tile, or tiles the
+    // pair skips), active after
+    run4(0, min(f + 1, n_t + 1), step_of(std::integral_constant<bool, false>{}));
+    run4(f + 1, n_t + 1, step_of(std::integral_constant<bool, true>{}));
+    // dK = scale * dK^T, dV = dV^T (lane = key, registers = head-dim index),
+    // stored as whole rows through one Q tile buffer per pair (free once
+    // every wave has left the tile loop; no copy is in flight)
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    sync::bare_barrier();
+    const int nrows = min(kBKV, p.Nk - k0);
+    const uint32_t range = (uint32_t)(nrows - 1) * row_bytes + 2 * D;
+    const auto out_k = make_rsrc(p.dk + kvo + (size_t)k0 * rs, range);
+    const auto out_v = make_rsrc(p.dv + kvo + (size_t)k0 * rs, range);
+    uint8_t* const slot = pair == 0 ? lds_q0 : pair == 1 ? lds_q1 : pair == 2 ? lds_q2 : lds_q3;
+    const uint32_t gbase = (uint32_t)(pair * 32) * row_bytes;
+    store_rows<O_, D>(dkt, -p.scale, slot, out_k, gbase, row_bytes, lane);  // dkt holds -dK^T
+    store_rows<O_, D>(dvt, 1.f, slot, out_v, gbase, row_bytes, lane);
+  }
+}
+
 }  // namespace mha
