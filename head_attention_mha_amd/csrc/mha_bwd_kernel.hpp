@@ -14,6 +14,9 @@
 //   (the FlashAttention long-sequence post, "Attention parallelism"; the
 //   SparkAttention backward passage): each wave owns 32 keys, streams the
 //   Q/dO tiles that see them and accumulates their dK and dV in registers.
+//   At d = 128, mha_bwd_dkdv_pair_kernel does the same work with two waves
+//   per 32 keys (a producer of P and dS and a consumer accumulating dK and
+//   dV), so that two waves share each SIMD.
 // * mha_bwd_dq_kernel: row-parallel, like the forward: each wave owns 32
 //   query rows and streams K/V tiles. The pages add dQ across column workers
 //   with atomics; "StreamKL" (Methodology section 2) also describes separate
