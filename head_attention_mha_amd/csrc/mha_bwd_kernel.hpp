@@ -105,6 +105,24 @@ struct Spread {
   }
 };
 
+// Query-side mask of a dK/dV tile. The lane's element r is query
+// qt0 + 8*hf + o with o = 16*(r>>3) + (r&7), a constant; it is visible iff
+// the query exists and (causal) does not precede the lane's key, i.e. iff o
+// lies in [lo, hi]. Held as a start and a width, so that one unsigned compare
+// of o - start decides it; an empty range gets a start no offset reaches.
+template <bool CAUSAL>
+struct QueryMask {
+  int start;
+  uint32_t width;
+  __device__ __forceinline__ QueryMask(int qt0, int hf, int my_k, int Nq) {
+    const int hi = Nq - 1 - qt0 - 8 * hf;
+    const int lo = CAUSAL ? my_k - qt0 - 8 * hf : 0;
+    start = hi >= lo ? lo : (1 << 30);
+    width = hi >= lo ? (uint32_t)(hi - lo) : 0u;
+  }
+  __device__ __forceinline__ bool visible(int o) const { return (uint32_t)(o - start) <= width; }
+};
+
 }  // namespace bwd
 
 // ---- D = rowsum(dO o O) ------------------------------------------------------
@@ -281,17 +299,15 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
       __builtin_amdgcn_sched_barrier(0);
       // P = exp(scale*s - LSE), dS = P o (dP - D); element r is key
       // j*BK + 32*kb + 16*(r>>3) + 8*hf + (r&7)
-      const int k0 = j * BK + kb * 32;
+      // visible iff key < Nk and (causal) key <= my_q: one per-lane limit
+      // on the element's offset 16*(r>>3) + (r&7), a constant
+      const int lim = (CAUSAL ? min(p.Nk - 1, my_q) : p.Nk - 1) - j * BK - kb * 32 - 8 * hf;
       u32x4 pf[2];
       float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
-        if constexpr (MASK) {
-          const int key = k0 + 16 * (r >> 3) + 8 * hf + (r & 7);
-          const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
-          pv = vis ? pv : 0.f;
-        }
+        if constexpr (MASK) pv = 16 * (r >> 3) + (r & 7) <= lim ? pv : 0.f;
         e[r] = pv * (dp[r] - dlt);
       }
 #pragma unroll
@@ -587,6 +603,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
     // dead by then: phase 1 and the seeding of dP' use them)
     constexpr int kLd = NM - kA - 2 * PK;
     const int qt0 = t * BQt;
+    const bwd::QueryMask<CAUSAL> qmask(qt0, hf, my_k, p.Nq);
 
     f32x16 s, dp;
 #pragma unroll
@@ -634,11 +651,7 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dkdv_kernel(BwdParams p
       bwd::static_for<SpreadP::lo(j), SpreadP::lo(j + 1)>([&](auto rt) __attribute__((always_inline)) {
         constexpr int r = decltype(rt)::value;
         float x = fast_exp2(__builtin_fmaf(s[r], c, nl[r]));
-        if constexpr (MASK) {
-          const int q = qt0 + 16 * (r >> 3) + 8 * hf + (r & 7);
-          const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
-          x = vis ? x : 0.f;
-        }
+        if constexpr (MASK) x = qmask.visible(16 * (r >> 3) + (r & 7)) ? x : 0.f;
         if constexpr (r & 1) {
           uint32_t w = O_::pack(pr[r - 1], x);
           asm volatile("s_nop 0" : "+v"(w));
@@ -1006,6 +1019,7 @@ __global__ __launch_bounds__(2 * bwd::kThreads) void mha_bwd_dkdv_pair_kernel(Bw
                     __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int qt0 = t * BQt;
+      const bwd::QueryMask<CAUSAL> qmask(qt0, hf, my_k, p.Nq);
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -1043,11 +1057,7 @@ __global__ __launch_bounds__(2 * bwd::kThreads) void mha_bwd_dkdv_pair_kernel(Bw
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               x[e] = fast_exp2(__builtin_fmaf(s[r + e], c, nl[r + e]));
-              if constexpr (MASK) {
-                const int q = qt0 + 16 * ((r + e) >> 3) + 8 * hf + ((r + e) & 7);
-                const bool vis = q < p.Nq && (!CAUSAL || my_k <= q);
-                x[e] = vis ? x[e] : 0.f;
-              }
+              if constexpr (MASK) x[e] = qmask.visible(16 * ((r + e) >> 3) + ((r + e) & 7)) ? x[e] : 0.f;
               pr[r + e] = x[e];
             }
             uint32_t w = O_::pack(x[0], x[1]);

@@ -590,13 +590,16 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       // the empty asm keeps the compiler from turning this rarely taken,
       // wave-uniform branch into selects executed on every tile
       asm volatile("" ::: "memory");
+      // element (kb, r) is key k0 + 8*hf + off with off = 32*kb + 16*(r>>3)
+      // + (r&7); it is visible iff key < Nk and (causal) key <= my_q, i.e.
+      // iff off <= lim: one compare with a constant per element
+      const int lim = (CAUSAL ? min(p.Nk - 1, my_q) : p.Nk - 1) - k0 - 8 * hf;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-          const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          const int off = kb * 32 + 16 * (r >> 3) + (r & 7);
+          s[kb][r] = off <= lim ? s[kb][r] : -INFINITY;
         }
     }
     // two independent max chains (one per 32-key block), then across halves

@@ -200,10 +200,12 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
         x2[r] = s2[r];
       }
       if constexpr (MASK) {
+        // visible iff key < Nk and (causal) key <= my_q: one per-lane limit
+        // on the element's offset 16*(r>>3) + (r&7), a constant
+        const int lim = (CAUSAL ? min(p.Nk - 1, my_q) : p.Nk - 1) - j * BK - kb * 32 - 8 * hf;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * BK + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-          const bool vis = key < p.Nk && (!CAUSAL || key <= my_q);
+          const bool vis = 16 * (r >> 3) + (r & 7) <= lim;
           x1[r] = vis ? x1[r] : NEG_INF;
           x2[r] = vis ? x2[r] : NEG_INF;
         }
