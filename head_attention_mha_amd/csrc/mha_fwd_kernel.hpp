@@ -146,6 +146,7 @@ struct Params {
 // The O rescale is deferred while a row's running max stays within 2^8 (in
 // the exp2 domain) of the reference max the accumulators were scaled to.
 constexpr float kDeferLog2 = 8.0f;
+constexpr float kDeferSum = 256.0f;  // 2^kDeferLog2
 
 // Row index of the K operand fed to MFMA row m: bits 2 and 3 of m swapped
 // (an involution).
@@ -602,39 +603,42 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
           s[kb][r] = off <= lim ? s[kb][r] : -INFINITY;
         }
     }
-    // two independent max chains (one per 32-key block), then across halves
-    float mk[KB];
+    // The exact step: row max of the tile (two independent chains, one per
+    // 32-key block, then across halves); the O and l rescale is deferred
+    // while the max stays within kDeferLog2 of the reference max m_run.
+    auto max_and_rescale = [&]() __attribute__((always_inline)) {
+      float mk[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      mk[kb] = s[kb][0];
+      for (int kb = 0; kb < KB; ++kb) {
+        mk[kb] = s[kb][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mk[kb] = fmaxf(mk[kb], s[kb][r]);
-    }
-    float mx = mk[0];
+        for (int r = 1; r < 16; ++r) mk[kb] = fmaxf(mk[kb], s[kb][r]);
+      }
+      float mx = mk[0];
 #pragma unroll
-    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mk[kb]);
-    mx = max_halves(mx);
-    // the O and l rescale is deferred while the max stays within
-    // kDeferLog2 of the reference max
-    if (__any(mx > m_run + p.defer_raw)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2((m_run - m_new) * c);
+      for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mk[kb]);
+      mx = max_halves(mx);
+      if (__any(mx > m_run + p.defer_raw)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2((m_run - m_new) * c);
 #pragma unroll
-      for (int e = 0; e < LP; ++e) l_run[e] *= alpha;
+        for (int e = 0; e < LP; ++e) l_run[e] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = m_run * c;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
-    // P^T fragments: k-step ks covers keys 16*ks + 8*hf + 0..7
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_run = m_new;
+      }
+    };
     if constexpr (LP == PK) {
-      // row sum straight into the PK running partial sums
+      max_and_rescale();
+      const float mc = m_run * c;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
+      // P^T fragments (k-step ks covers keys 16*ks + 8*hf + 0..7), the row
+      // sum straight into the PK running partial sums
 #pragma unroll
       for (int ks = 0; ks < PK; ++ks) {
         const int kb = ks >> 1, r0 = 8 * (ks & 1);
@@ -645,21 +649,47 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
         }
       }
     } else {
-      // row sum of the tile in PK independent chains (one per k-step)
-      float rsum[PK];
+      // P = exp(scale*(s - m_run)) into the P^T fragments (k-step ks covers
+      // keys 16*ks + 8*hf + 0..7), leaving s as it is; returns the lane's
+      // part of the tile's row sum (PK independent chains)
+      auto exp_pack = [&]() __attribute__((always_inline)) -> float {
+        const float mc = m_run * c;
+        float rsum[PK];
 #pragma unroll
-      for (int ks = 0; ks < PK; ++ks) {
-        const int kb = ks >> 1, r0 = 8 * (ks & 1);
-        rsum[ks] = 0.f;
+        for (int ks = 0; ks < PK; ++ks) {
+          const int kb = ks >> 1, r0 = 8 * (ks & 1);
+          rsum[ks] = 0.f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          pf[ks][t] = O_::pack(s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1]);
-          rsum[ks] = O_::sum2(pf[ks][t], s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1], rsum[ks]);
+          for (int t = 0; t < 4; ++t) {
+            const float x0 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2 * t], c, -mc));
+            const float x1 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2 * t + 1], c, -mc));
+            pf[ks][t] = O_::pack(x0, x1);
+            rsum[ks] = O_::sum2(pf[ks][t], x0, x1, rsum[ks]);
+          }
         }
-      }
 #pragma unroll
-      for (int ks = 1; ks < PK; ++ks) rsum[0] += rsum[ks];
-      l_run[0] += rsum[0];
+        for (int ks = 1; ks < PK; ++ks) rsum[0] += rsum[ks];
+        return rsum[0];
+      };
+      // The row max only decides whether the reference max moves, i.e.
+      // whether some score exceeds m_run by more than the deferral bound.
+      // Every P is at most the lane's tile sum, so a sum within 2^kDeferLog2
+      // on every lane shows that no score crossed the bound, and the max is
+      // not needed: the P taken against m_run are those the exact step gives.
+      // Otherwise (and on the first tile, before m_run is set) the exact
+      // step runs and P is taken again. The test is written so that a NaN
+      // or infinite sum (scores far past m_run) fails it.
+      bool exact = j == 0;
+      float rt = 0.f;
+      if (!exact) {
+        rt = exp_pack();
+        exact = __any(!(rt <= kDeferSum));
+      }
+      if (exact) {
+        max_and_rescale();
+        rt = exp_pack();
+      }
+      l_run[0] += rt;
     }
   };
 
