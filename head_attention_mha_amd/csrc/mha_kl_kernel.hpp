@@ -210,52 +210,91 @@ __global__ __launch_bounds__(kl::kThreads) void mha_kl_kernel(KlParams p) {
           x2[r] = vis ? x2[r] : NEG_INF;
         }
       }
-      // chains started from -inf: the compiler then forms three-input
-      // maxima throughout, with no NaN-quieting copies of the raw scores
-      float t1 = NEG_INF, t2 = NEG_INF;
+      // The exact step: block maxima (chains started from -inf, so that the
+      // compiler forms three-input maxima throughout, with no NaN-quieting
+      // copies of the raw scores), merged over the two halves, and the
+      // deferred rescale of whichever distribution's maximum outgrew its
+      // reference by more than the bound.
+      auto max_and_rescale = [&]() __attribute__((always_inline)) {
+        float t1 = NEG_INF, t2 = NEG_INF;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        t1 = fmaxf(t1, x1[r]);
-        t2 = fmaxf(t2, x2[r]);
-      }
-      t1 = kl::max_halves3(t1);
-      t2 = kl::max_halves3(t2);
-      // A row that sees no key of this block (causal, diagonal tile) has
-      // t = -inf and never moves its maximum here; while a row has seen no
-      // key at all its m * c stays 0, so masked weights are exp2(-inf) = 0.
-      const bool g1 = t1 > m1 + p.defer_raw, g2 = t2 > m2 + p.defer_raw;
-      if (__any(g1 || g2)) {
-        // the wave-uniform branch is rare after the first blocks
-        asm volatile("" ::: "memory");
-        if (g1) {
-          const float al = fast_exp2((m1 - t1) * c);  // 0 when m1 = -inf
-          m1 = t1;
-          m1c = t1 * c;
+        for (int r = 0; r < 16; ++r) {
+          t1 = fmaxf(t1, x1[r]);
+          t2 = fmaxf(t2, x2[r]);
+        }
+        t1 = kl::max_halves3(t1);
+        t2 = kl::max_halves3(t2);
+        // A row that sees no key of this block (causal, diagonal tile) has
+        // t = -inf and never moves its maximum here; while a row has seen no
+        // key at all its m * c stays 0, so masked weights are exp2(-inf) = 0.
+        const bool g1 = t1 > m1 + p.defer_raw, g2 = t2 > m2 + p.defer_raw;
+        if (__any(g1 || g2)) {
+          // the wave-uniform branch is rare after the first blocks
+          asm volatile("" ::: "memory");
+          if (g1) {
+            const float al = fast_exp2((m1 - t1) * c);  // 0 when m1 = -inf
+            m1 = t1;
+            m1c = t1 * c;
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            l1[e] *= al;
-            acc[e] *= al;
+            for (int e = 0; e < 2; ++e) {
+              l1[e] *= al;
+              acc[e] *= al;
+            }
+          }
+          if (g2) {
+            const float al = fast_exp2((m2 - t2) * c);
+            m2 = t2;
+            m2c = t2 * c;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) l2[e] *= al;
           }
         }
-        if (g2) {
-          const float al = fast_exp2((m2 - t2) * c);
-          m2 = t2;
-          m2c = t2 * c;
+      };
+      // The block's weights against the reference maxima, summed in two
+      // chains each (even and odd elements) that start from the block's
+      // first elements; the raw scores stay as they are.
+      float b1[2], b2[2], ba[2];
+      auto block_sums = [&]() __attribute__((always_inline)) {
 #pragma unroll
-          for (int e = 0; e < 2; ++e) l2[e] *= al;
+        for (int r = 0; r < 16; ++r) {
+          const float p1 = fast_exp2(__builtin_fmaf(x1[r], c, -m1c));
+          const float p2 = fast_exp2(__builtin_fmaf(x2[r], c, -m2c));
+          // the difference of the raw (unmasked, finite) scores; the scale
+          // is applied to acc once at the end. Exactly 0 where the two
+          // scores are equal.
+          const float dx = s1[r] - s2[r];
+          if (r < 2) {
+            b1[r] = p1;
+            b2[r] = p2;
+            ba[r] = p1 * dx;
+          } else {
+            b1[r & 1] += p1;
+            b2[r & 1] += p2;
+            ba[r & 1] = __builtin_fmaf(p1, dx, ba[r & 1]);
+          }
         }
+      };
+      // The maxima only decide whether a reference moves, i.e. whether some
+      // score exceeds it by more than the deferral bound. Every weight is at
+      // most its lane's block sum, so sums within 2^kDeferLog2 on every lane
+      // show that no score crossed the bound and the maxima are not needed.
+      // Otherwise the exact step runs and the block is summed again; so
+      // does the first block, which sets both references (every row sees
+      // key 0). The test is written so that a NaN or infinite sum fails it.
+      bool exact = kb == 0 && j == 0;
+      if (!exact) {
+        block_sums();
+        exact = __any(!(b1[0] + b1[1] <= kDeferSum) || !(b2[0] + b2[1] <= kDeferSum));
+      }
+      if (exact) {
+        max_and_rescale();
+        block_sums();
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p1 = fast_exp2(__builtin_fmaf(x1[r], c, -m1c));
-        const float p2 = fast_exp2(__builtin_fmaf(x2[r], c, -m2c));
-        // the difference of the raw (unmasked, finite) scores; the scale is
-        // applied to acc once at the end. Exactly 0 where the two scores are
-        // equal.
-        const float dx = s1[r] - s2[r];
-        l1[r & 1] += p1;
-        l2[r & 1] += p2;
-        acc[r & 1] = __builtin_fmaf(p1, dx, acc[r & 1]);
+      for (int e = 0; e < 2; ++e) {
+        l1[e] += b1[e];
+        l2[e] += b2[e];
+        acc[e] += ba[e];
       }
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -118,11 +118,34 @@ def test_kl_shapes(torch_mod, mha, case):
     check(torch_mod, mha, q1, k1, q2, k2, dtype, causal, scale, label=str(case))
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-def test_kl_far_apart(torch_mod, mha, dtype):
-    """Unrelated distributions with peaky rows (noise 3, scale 0.25): large KL."""
-    q1, k1, q2, k2 = _inputs(1, 2, 300, 700, 64, dtype, 71, noise=3.0)
-    check(torch_mod, mha, q1, k1, q2, k2, dtype, True, 0.25, label=f"far-{dtype}")
+@pytest.mark.parametrize("d,dtype", [(64, "fp16"), (64, "bf16"), (128, "bf16"), (128, "fp16")])
+def test_kl_far_apart(torch_mod, mha, d, dtype):
+    """Unrelated distributions with peaky rows (noise 3, scale 0.25 at d = 64,
+    0.125 at d = 128): large KL, and reference maxima that move often."""
+    q1, k1, q2, k2 = _inputs(1, 2, 300, 700, d, dtype, 71, noise=3.0)
+    check(torch_mod, mha, q1, k1, q2, k2, dtype, True, 0.25 if d == 64 else 0.125,
+          label=f"far-d{d}-{dtype}")
+
+
+@pytest.mark.parametrize("d,dtype,c", [(128, "bf16", 2048.0), (64, "fp16", 1024.0)])
+def test_kl_score_jump(torch_mod, mha, d, dtype, c):
+    """Each distribution has one key far above the others (c * scale = 181
+    and 128 nats), late in the keys and in different 32-key blocks (150 for
+    P2, 190 for P1): the weights taken against the reference maxima set by
+    the earlier keys overflow fp32 there (above 2^128 in the exp2 domain),
+    so the kernel must fall back to its exact maximum step. KL is then about
+    c * scale (P1 sits on key 190, where P2 is tiny)."""
+    B, H, Nq, Nk = 1, 1, 130, 200
+    q = np.zeros((B, Nq, H, d))
+    q[..., 0] = c
+    k1 = np.zeros((B, Nk, H, d))
+    k2 = np.zeros((B, Nk, H, d))
+    k1[:, 190, :, 0] = 1.0
+    k2[:, 150, :, 0] = 1.0
+    bits = [wl.round_bits(np.asarray(x, np.float32), dtype) for x in (q, k1, q, k2)]
+    scale = 1 / math.sqrt(d)
+    st, (kl, _, _) = check(torch_mod, mha, *bits, dtype, False, scale, label=f"jump-d{d}-{dtype}")
+    assert np.abs(kl - c * np.float32(scale)).max() <= 1e-2
 
 
 @pytest.mark.parametrize("name", list(wl.KL_WORKLOADS))
