@@ -511,13 +511,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
 #pragma unroll
   for (int ks = 0; ks < PK; ++ks) pf[ks] = u32x4{0, 0, 0, 0};
   float m_run = -INFINITY;  // reference max (raw scores q.k) of o and l_run
-  // this lane's part of the row sum: at d = 64, PK running partial sums fed
-  // straight from the packing (no per-tile seed or combine; 3-4 % faster at
-  // d = 64), at d = 128 one sum (the partial sums cost 2-3 % there)
-  constexpr int LP = D == 64 ? PK : 1;
-  float l_run[LP];
-#pragma unroll
-  for (int e = 0; e < LP; ++e) l_run[e] = 0.f;
+  float l_run = 0.f;        // this lane's part of the row sum
   const float c = p.scale_log2;
 
   // GEMM phase of tile j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T.
@@ -621,8 +615,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       if (__any(mx > m_run + p.defer_raw)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2((m_run - m_new) * c);
-#pragma unroll
-        for (int e = 0; e < LP; ++e) l_run[e] *= alpha;
+        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -630,67 +623,50 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
         m_run = m_new;
       }
     };
-    if constexpr (LP == PK) {
-      max_and_rescale();
+    // P = exp(scale*(s - m_run)) into the P^T fragments (k-step ks covers
+    // keys 16*ks + 8*hf + 0..7), leaving s as it is; returns the lane's
+    // part of the tile's row sum (PK independent chains)
+    auto exp_pack = [&]() __attribute__((always_inline)) -> float {
       const float mc = m_run * c;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
-      // P^T fragments (k-step ks covers keys 16*ks + 8*hf + 0..7), the row
-      // sum straight into the PK running partial sums
+      float rsum[PK];
 #pragma unroll
       for (int ks = 0; ks < PK; ++ks) {
         const int kb = ks >> 1, r0 = 8 * (ks & 1);
+        // (chains from 0: seeding them with the first pair saves an add
+        // but changes the compiler's order of the exponentials, packs and
+        // adds, which measured 2 % slower at d = 128)
+        rsum[ks] = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          pf[ks][t] = O_::pack(s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1]);
-          l_run[ks] = O_::sum2(pf[ks][t], s[kb][r0 + 2 * t], s[kb][r0 + 2 * t + 1], l_run[ks]);
+          const float x0 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2 * t], c, -mc));
+          const float x1 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2 * t + 1], c, -mc));
+          pf[ks][t] = O_::pack(x0, x1);
+          rsum[ks] = O_::sum2(pf[ks][t], x0, x1, rsum[ks]);
         }
       }
-    } else {
-      // P = exp(scale*(s - m_run)) into the P^T fragments (k-step ks covers
-      // keys 16*ks + 8*hf + 0..7), leaving s as it is; returns the lane's
-      // part of the tile's row sum (PK independent chains)
-      auto exp_pack = [&]() __attribute__((always_inline)) -> float {
-        const float mc = m_run * c;
-        float rsum[PK];
 #pragma unroll
-        for (int ks = 0; ks < PK; ++ks) {
-          const int kb = ks >> 1, r0 = 8 * (ks & 1);
-          rsum[ks] = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float x0 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2 * t], c, -mc));
-            const float x1 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2 * t + 1], c, -mc));
-            pf[ks][t] = O_::pack(x0, x1);
-            rsum[ks] = O_::sum2(pf[ks][t], x0, x1, rsum[ks]);
-          }
-        }
-#pragma unroll
-        for (int ks = 1; ks < PK; ++ks) rsum[0] += rsum[ks];
-        return rsum[0];
-      };
-      // The row max only decides whether the reference max moves, i.e.
-      // whether some score exceeds m_run by more than the deferral bound.
-      // Every P is at most the lane's tile sum, so a sum within 2^kDeferLog2
-      // on every lane shows that no score crossed the bound, and the max is
-      // not needed: the P taken against m_run are those the exact step gives.
-      // Otherwise (and on the first tile, before m_run is set) the exact
-      // step runs and P is taken again. The test is written so that a NaN
-      // or infinite sum (scores far past m_run) fails it.
-      bool exact = j == 0;
-      float rt = 0.f;
-      if (!exact) {
-        rt = exp_pack();
-        exact = __any(!(rt <= kDeferSum));
-      }
-      if (exact) {
-        max_and_rescale();
-        rt = exp_pack();
-      }
-      l_run[0] += rt;
+      for (int ks = 1; ks < PK; ++ks) rsum[0] += rsum[ks];
+      return rsum[0];
+    };
+    // The row max only decides whether the reference max moves, i.e.
+    // whether some score exceeds m_run by more than the deferral bound.
+    // Every P is at most the lane's tile sum, so a sum within 2^kDeferLog2
+    // on every lane shows that no score crossed the bound, and the max is
+    // not needed: the P taken against m_run are those the exact step gives.
+    // Otherwise (and on the first tile, before m_run is set) the exact
+    // step runs and P is taken again. The test is written so that a NaN
+    // or infinite sum (scores far past m_run) fails it.
+    bool exact = j == 0;
+    float rt = 0.f;
+    if (!exact) {
+      rt = exp_pack();
+      exact = __any(!(rt <= kDeferSum));
     }
+    if (exact) {
+      max_and_rescale();
+      rt = exp_pack();
+    }
+    l_run += rt;
   };
 
   // ---- period schedule -----------------------------------------------------
@@ -819,10 +795,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   // chunk c at c ^ (ln mod CH) so the writes spread over the banks) and
   // leave as 16-byte stores that cover whole rows. The buffer's range check
   // drops rows past Nq.
-  float l_lane = l_run[0];
-#pragma unroll
-  for (int e = 1; e < LP; ++e) l_lane += l_run[e];
-  const float l_tot = sum_halves(l_lane);
+  const float l_tot = sum_halves(l_run);
   const float inv = 1.f / l_tot;
   {
     const int nrows = min(kBQ, p.Nq - q0);
