@@ -8,7 +8,9 @@
 //   2. masks scores only on tiles that cross the causal diagonal or the end
 //      of the keys; tiles wholly past the causal frontier are never loaded;
 //   3. online softmax: running row max m and row sum l, O rescaled by
-//      alpha = exp(scale*(m_old - m_new)) when the max has grown;
+//      alpha = exp(scale*(m_old - m_new)) when the max has grown (the
+//      tile's row max itself is taken only when its P, computed against
+//      the running max first, sum past the deferral bound below);
 //   4. converts P to bf16/f16 in registers and accumulates O^T += V^T . P^T
 //      on MFMA.
 // After the last tile O is divided by l, rounded to the I/O type and written
@@ -56,6 +58,9 @@
 // * The O rescale is deferred while a row's max stays within 2^8 (exp2
 //   domain) of the max O and l were last scaled to; O/l and LSE are the same
 //   in exact arithmetic, and the rescale then runs only when the max jumps.
+//   Since every P is at most its lane's tile sum, a tile whose sums stay
+//   within 2^8 needs no row max at all; element masks are one compare of
+//   a constant offset with a per-lane limit.
 // * The 1-D grid is remapped so that all query tiles of a head run on one
 //   XCD (workgroups are dispatched round-robin over the 8 XCDs), keeping the
 //   head's K/V in that XCD's L2; heads are taken in groups small enough for

@@ -6,8 +6,9 @@
 // ("StreamKL", Methodology section 1). Each row keeps five running scalars:
 // reference maxima m1, m2 of the two score rows, the sums l1, l2 of
 // exp(S_t - m_t) and acc = sum_j exp(S1_ij - m1)(S1_ij - S2_ij), all rescaled
-// when a maximum outgrows its reference by more than 2^8 (exp2 domain); at the end KL = acc / l1 + LSE2 - LSE1 with
-// LSE_t = m_t + log l_t. There is no P.V product: acc is one number per row,
+// when a maximum outgrows its reference by more than 2^8 (exp2 domain; the
+// block maxima are taken only for blocks whose weights sum past that
+// bound); at the end KL = acc / l1 + LSE2 - LSE1 with LSE_t = m_t + log l_t. There is no P.V product: acc is one number per row,
 // not a row of an output matrix.
 //
 // Structure as the row-parallel kernels of this library: 4 waves per
