@@ -1,7 +1,7 @@
 """Benchmark of the fused MHA forward (default) or backward on one MI355X.
 
 A step is one mha_fwd call (``--pass fwd``) or one mha_bwd call (``--pass
-bwd``: D, dQ and dK/dV, from the forward's O and LSE computed beforehand)
+bwd``: dQ with D, then dK/dV, from the forward's O and LSE computed beforehand)
 over the whole workload, inputs already resident in HBM. After the W
 warm-up steps, untimed steps run for SETTLE_S seconds (the engine clock
 ramps up under load); then K steps run back to back between two events on
@@ -584,7 +584,7 @@ def cpu_baseline_proj(w, ob, wb, bb, target_s: float) -> dict:
 # clock). The timed launches of a child are found from the settle count it
 # prints; their mean per step is reported.
 STEP_KERNELS = {"fwd": ["mha_fwd_kernel"],
-                "bwd": ["mha_bwd_delta_kernel", "mha_bwd_dq_kernel", "mha_bwd_dkdv_kernel"],
+                "bwd": ["mha_bwd_dq_kernel", "mha_bwd_dkdv_kernel", "mha_bwd_dkdv_pair_kernel"],
                 "splitkv": ["mha_split_partial_kernel", "mha_split_merge_kernel"],
                 "kl": ["mha_kl_kernel"], "proj": ["mha_proj_kernel"]}
 LIVE_SQ = ["SQ_WAVES", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
@@ -659,7 +659,8 @@ def live_counters(which: str, workload: str) -> dict:
             tot = 0.0
             for k in STEP_KERNELS[which]:
                 t = _timed(ds, k, line, steps)
-                tot += sum(d[ctr] for d in t) / len(t) * 1024 * factor
+                if t:  # (one of the dK/dV kernels, by head size)
+                    tot += sum(d[ctr] for d in t) / len(t) * 1024 * factor
             per[ctr] = tot
             out[f"{ctr.lower()}_calibration_factor"] = round(factor, 4)
         out["fetch_bytes_per_step"] = round(per["FETCH_SIZE"])
@@ -671,6 +672,8 @@ def live_counters(which: str, workload: str) -> dict:
             kern = {}
             for k in STEP_KERNELS[which]:
                 t = _timed(ds, k, line, steps)
+                if not t:
+                    continue
                 dur = sum(d["end"] - d["start"] for d in t) / len(t)
                 busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in t) / len(t) / N_SIMD
                 grbm = sum(d["GRBM_GUI_ACTIVE"] for d in t) / len(t) / N_XCD
@@ -880,7 +883,7 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel": {"fwd": "mha_fwd_kernel", "kl": "mha_kl_kernel",
-                           "bwd": "mha_bwd (delta, dq and dkdv kernels, one call)"}[args.which]}
+                           "bwd": "mha_bwd (dq with D, then dkdv, one call)"}[args.which]}
         if dev["peak_tflops_from_device"]:
             roof["peak_from_device"] = dev["peak_tflops_from_device"]
             roof["frac_of_device_peak"] = round(achieved / dev["peak_tflops_from_device"], 4)

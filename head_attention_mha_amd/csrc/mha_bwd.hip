@@ -1,6 +1,6 @@
-// C ABI of the attention backward: template dispatch and launch of the D, dQ
-// and dK/dV kernels (contract in include/mha.h; argument checks in
-// mha_validate.hpp).
+// C ABI of the attention backward: template dispatch and launch of the dQ
+// kernel (which also forms D) and the dK/dV kernel (contract in
+// include/mha.h; argument checks in mha_validate.hpp).
 #include "mha_bwd_kernel.hpp"
 #include "mha_common.hpp"
 
@@ -9,18 +9,15 @@ using namespace mha_host;
 namespace {
 
 template <typename T, int D, bool C>
-mha_status_t launch_bwd(const mha::BwdParams& pd, const mha::BwdParams& pq,
-                        const mha::BwdParams& pk, bool run_q, bool run_k, hipStream_t stream) {
+mha_status_t launch_bwd(const mha::BwdParams& pq, const mha::BwdParams& pk, bool run_q, bool run_k,
+                        hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (run_q) {
-    void* a0[] = {const_cast<mha::BwdParams*>(&pd)};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&mha::mha_bwd_delta_kernel<T, D>),
-                        dim3(pd.n_blocks), dim3(mha::bwd::kThreads), a0, 0, stream);
-    if (e == hipSuccess) {
-      void* a1[] = {const_cast<mha::BwdParams*>(&pq)};
-      e = hipLaunchKernel(reinterpret_cast<const void*>(&mha::mha_bwd_dq_kernel<T, D, C>),
-                          dim3(pq.n_blocks), dim3(mha::bwd::kThreads), a1, 0, stream);
-    }
+    // dQ and D (the dK/dV kernel, launched after it on the same stream,
+    // reads D)
+    void* a1[] = {const_cast<mha::BwdParams*>(&pq)};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&mha::mha_bwd_dq_kernel<T, D, C>),
+                        dim3(pq.n_blocks), dim3(mha::bwd::kThreads), a1, 0, stream);
   }
   if (e == hipSuccess && run_k) {
     void* a2[] = {const_cast<mha::BwdParams*>(&pk)};
@@ -41,14 +38,13 @@ mha_status_t launch_bwd(const mha::BwdParams& pd, const mha::BwdParams& pq,
 }
 
 template <typename T>
-mha_status_t dispatch_bwd(const mha::BwdParams& pd, const mha::BwdParams& pq,
-                          const mha::BwdParams& pk, bool run_q, bool run_k, int d, bool causal,
-                          hipStream_t s) {
+mha_status_t dispatch_bwd(const mha::BwdParams& pq, const mha::BwdParams& pk, bool run_q, bool run_k,
+                          int d, bool causal, hipStream_t s) {
   if (d == 64)
-    return causal ? launch_bwd<T, 64, true>(pd, pq, pk, run_q, run_k, s)
-                  : launch_bwd<T, 64, false>(pd, pq, pk, run_q, run_k, s);
-  return causal ? launch_bwd<T, 128, true>(pd, pq, pk, run_q, run_k, s)
-                : launch_bwd<T, 128, false>(pd, pq, pk, run_q, run_k, s);
+    return causal ? launch_bwd<T, 64, true>(pq, pk, run_q, run_k, s)
+                  : launch_bwd<T, 64, false>(pq, pk, run_q, run_k, s);
+  return causal ? launch_bwd<T, 128, true>(pq, pk, run_q, run_k, s)
+                : launch_bwd<T, 128, false>(pq, pk, run_q, run_k, s);
 }
 
 }  // namespace
@@ -83,11 +79,7 @@ mha_status_t mha_bwd(const void* q, const void* k, const void* v, const void* o,
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
 
-  mha::BwdParams pd = p, pq = p, pk = p;
-  const long long n_rows = (long long)B * H * Nq;
-  const int rows_per_block = mha::bwd::kThreads / (d / 8);
-  pd.n_tiles = 0;
-  pd.n_blocks = (int)((n_rows + rows_per_block - 1) / rows_per_block);
+  mha::BwdParams pq = p, pk = p;
   pq.n_tiles = (Nq + mha::bwd::kBQ - 1) / mha::bwd::kBQ;
   pq.n_blocks = B * H * pq.n_tiles;
   pk.n_tiles = (Nk + mha::bwd::kBKV - 1) / mha::bwd::kBKV;
@@ -96,8 +88,8 @@ mha_status_t mha_bwd(const void* q, const void* k, const void* v, const void* o,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool run_q = !empty_q, run_k = !empty_k;
   if (dtype == MHA_DTYPE_BF16)
-    return dispatch_bwd<mha::BF16>(pd, pq, pk, run_q, run_k, d, causal != 0, s);
-  return dispatch_bwd<mha::F16>(pd, pq, pk, run_q, run_k, d, causal != 0, s);
+    return dispatch_bwd<mha::BF16>(pq, pk, run_q, run_k, d, causal != 0, s);
+  return dispatch_bwd<mha::F16>(pq, pk, run_q, run_k, d, causal != 0, s);
 }
 
 }  // extern "C"

@@ -9,7 +9,6 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Three kernels, each owning its outputs (no atomics, no workspace):
-// * mha_bwd_delta_kernel: D, one group of d/8 lanes per query row.
 // * mha_bwd_dkdv_kernel: column-parallel, as the pages' backward workers are
 //   (the FlashAttention long-sequence post, "Attention parallelism"; the
 //   SparkAttention backward passage): each wave owns 32 keys, streams the
@@ -125,38 +124,6 @@ struct QueryMask {
 
 }  // namespace bwd
 
-// ---- D = rowsum(dO o O) ------------------------------------------------------
-// One group of D/8 lanes per query row (16 bytes per lane, contiguous), rows
-// ordered as D is stored: r = (b*H + h)*Nq + i.
-template <typename T, int D>
-__global__ __launch_bounds__(bwd::kThreads) void mha_bwd_delta_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;                    // lanes per row
-  constexpr int RPB = bwd::kThreads / LPR;      // rows per workgroup
-  const int tid = threadIdx.x;
-  const long long row = (long long)blockIdx.x * RPB + tid / LPR;
-  const long long n_rows = (long long)p.B * p.H * p.Nq;
-  const int part = tid % LPR;
-  float acc = 0.f;
-  if (row < n_rows) {
-    const long long bh = row / p.Nq;
-    const int i = (int)(row - bh * p.Nq);
-    const int b = (int)(bh / p.H), h = (int)(bh - (long long)b * p.H);
-    const size_t off = (((size_t)b * p.Nq + i) * p.H + h) * D + 8 * part;
-    const u32x4 ov = *reinterpret_cast<const u32x4*>(p.o + off);
-    const u32x4 gv = *reinterpret_cast<const u32x4*>(p.dout + off);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const f32x2 a = bwd::unpack2<T>(ov[w]);
-      const f32x2 g = bwd::unpack2<T>(gv[w]);
-      acc = __builtin_fmaf(a[0], g[0], acc);
-      acc = __builtin_fmaf(a[1], g[1], acc);
-    }
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < n_rows && part == 0) p.delta[row] = acc;
-}
-
 // ---- dQ: row-parallel ----------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) {
@@ -207,23 +174,37 @@ __global__ __launch_bounds__(bwd::kThreads) void mha_bwd_dq_kernel(BwdParams p) 
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + ln;
 
-  // Q and dO fragments (B operands), read once; LSE (log2 units) and D
+  // Q and dO fragments (B operands), read once; LSE (log2 units); and
+  // D = rowsum(dO o O), formed here from the same elements of O as the lane
+  // holds of dO (half a row: lanes l and l ^ 32 share a row) and written
+  // out for the dK/dV kernel, which runs after this one
   u32x4 qf[DK], gf[DK];
-  float lse2 = 0.f, dlt = 0.f;
+  float lse2 = 0.f, dpart = 0.f;
   if (my_q < p.Nq) {
     const uint16_t* qrow = p.q + qo + (size_t)my_q * rs + 8 * hf;
     const uint16_t* grow = p.dout + qo + (size_t)my_q * rs + 8 * hf;
+    const uint16_t* orow = p.o + qo + (size_t)my_q * rs + 8 * hf;
 #pragma unroll
     for (int i = 0; i < DK; ++i) {
       qf[i] = *reinterpret_cast<const u32x4*>(qrow + 16 * i);
       gf[i] = *reinterpret_cast<const u32x4*>(grow + 16 * i);
+      const u32x4 ov = *reinterpret_cast<const u32x4*>(orow + 16 * i);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t gw = gf[i][w], ow = ov[w];
+        const f32x2 a = bwd::unpack2<T>(ow);
+        const f32x2 g = bwd::unpack2<T>(gw);
+        dpart = __builtin_fmaf(a[0], g[0], dpart);
+        dpart = __builtin_fmaf(a[1], g[1], dpart);
+      }
     }
     lse2 = p.lse[(size_t)bh * p.Nq + my_q] * bwd::kLog2e;
-    dlt = p.delta[(size_t)bh * p.Nq + my_q];
   } else {
 #pragma unroll
     for (int i = 0; i < DK; ++i) qf[i] = gf[i] = u32x4{0, 0, 0, 0};
   }
+  const float dlt = sum_halves(dpart);
+  if (hf == 0 && my_q < p.Nq) p.delta[(size_t)bh * p.Nq + my_q] = dlt;
 
   // key tiles
   const int n_ktiles_all = (p.Nk + BK - 1) / BK;
