@@ -317,27 +317,28 @@ __device__ __forceinline__ void store_rows(const f32x16* acc, float mul, uint8_t
   }
 }
 
-// Scheduling pins for the GEMM phase: the reads of the first AHEAD operands,
-// then for every MFMA n one MFMA followed by the 16-byte read of operand
+// Scheduling pins for a GEMM phase that runs MFMAs N .. NE-1 (the first NPV
+// take two operand reads, the rest one): the reads of the first AHEAD
+// operands, then for every MFMA n one MFMA followed by the reads of operand
 // n+AHEAD.
-template <int N, int NPV, int NS, int AHEAD>
+template <int N, int NPV, int NE, int AHEAD>
 struct PinInterleave {
   static constexpr int reads_of(int n) { return n < NPV ? 2 : 1; }
+  // the reads before MFMA N (the phase's first)
   static constexpr int preload() {
     int r = 0;
-    for (int n = 0; n < AHEAD; ++n) r += reads_of(n);
+    for (int n = N; n < N + AHEAD && n < NE; ++n) r += reads_of(n);
     return r;
   }
-  // region before the first MFMA: the first operand reads
   static __device__ __forceinline__ void pin_preload() {
     __builtin_amdgcn_sched_group_barrier(0x100, preload(), 0);
   }
   static __device__ __forceinline__ void apply() {
-    if constexpr (N < NPV + NS) {
+    if constexpr (N < NE) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (N + AHEAD < NPV + NS)
+      if constexpr (N + AHEAD < NE)
         __builtin_amdgcn_sched_group_barrier(0x100, reads_of(N + AHEAD), 0);
-      PinInterleave<N + 1, NPV, NS, AHEAD>::apply();
+      PinInterleave<N + 1, NPV, NE, AHEAD>::apply();
     }
   }
 };
@@ -528,13 +529,15 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
   constexpr int NPV = PK * DB;  // P.V MFMAs per tile
   constexpr int NS = DK * KB;   // S^T MFMAs per tile
   constexpr int kAhead = 3;
-  // One code path for every GEMM phase (distinct paths would each keep O in
-  // their own registers and copy it across on every tile): for j = 0 the
-  // P.V MFMAs multiply P = 0 with a zero-filled V buffer, and for j = j_end
-  // the S^T MFMAs produce a tile nobody reads.
+  // The phase of tile 0 has no P.V part and a wave's phase j = j_end, after
+  // its last tile, no S^T part (KIND 1 and 2, compile time); the middle
+  // phases share one code path, so O stays in the same registers throughout.
   // `copies` issues this wave's tile copies right after the first operand
   // reads (their latency hides the issue) and before the first MFMA.
-  auto gemm = [&](int j, const uint8_t* lk, const uint8_t* lv, auto copies) __attribute__((always_inline)) {
+  auto gemm = [&](int j, const uint8_t* lk, const uint8_t* lv, auto copies, auto kind)
+                  __attribute__((always_inline)) {
+    constexpr int N0 = decltype(kind)::value == 1 ? NPV : 0;         // first MFMA
+    constexpr int NE = decltype(kind)::value == 2 ? NPV : NPV + NS;  // one past the last
     uint32_t ko[DK];
 #pragma unroll
     for (int i = 0; i < DK; ++i) {
@@ -558,18 +561,20 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     // past its rows discards the operands), so the copies appear once
     u32x4 buf[kAhead];
 #pragma unroll
-    for (int n = 0; n < kAhead; ++n) buf[n] = load_op(n);
+    for (int n = N0; n < N0 + kAhead && n < NE; ++n) buf[n % kAhead] = load_op(n);
     copies();
-    PinInterleave<0, NPV, NS, kAhead>::pin_preload();
+    PinInterleave<N0, NPV, NE, kAhead>::pin_preload();
     if (j > j_end) return;  // wave-uniform: past this wave's rows
+    if constexpr (NE > NPV) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    }
 #pragma unroll
-    for (int n = 0; n < NPV + NS; ++n) {
+    for (int n = N0; n < NE; ++n) {
       const u32x4 a = buf[n % kAhead];
-      if (n + kAhead < NPV + NS) buf[n % kAhead] = load_op(n + kAhead);
+      if (n + kAhead < NE) buf[n % kAhead] = load_op(n + kAhead);
       if (n < NPV) {
         const int ks = n / DB, db = n % DB;
         o[db] = O_::mfma(a, pf[ks], o[db]);
@@ -579,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       }
     }
     // pin the order: per MFMA the reads kAhead ahead
-    PinInterleave<0, NPV, NS, kAhead>::apply();
+    PinInterleave<N0, NPV, NE, kAhead>::apply();
   };
 
   // Softmax phase of tile j: mask, running max, exp, row sum, P^T fragments.
@@ -725,52 +730,65 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
     }
   };
   auto no_copies = []() __attribute__((always_inline)) {};
-  // GEMM phase of tile j with BUF = j & 1: K_j in K buffer BUF, V_{j-1} in
-  // V buffer BUF ^ 1.
-  auto gemm_phase = [&](int j, auto buf, auto copies) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(2);
-    if constexpr (decltype(buf)::value == 0)
-      gemm(j, lds_k0, lds_v1, copies);
-    else
-      gemm(j, lds_k1, lds_v0, copies);
-    __builtin_amdgcn_s_setprio(0);
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // GEMM phase of tile j with BUF = j & 1: K_j in K buffer BUF, V_{j-1} in
+  // V buffer BUF ^ 1; KIND as for gemm (default: a middle phase).
+  auto gemm_phase = [&](int j, auto buf, auto copies, auto kind) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(2);
+    if constexpr (decltype(buf)::value == 0)
+      gemm(j, lds_k0, lds_v1, copies, kind);
+    else
+      gemm(j, lds_k1, lds_v0, copies, kind);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-  // the first GEMM phase multiplies P = 0 with V buffer 1: make it finite
-  for (int i = tid; i < TILEB / 16; i += kThreads)
-    reinterpret_cast<u32x4*>(lds_v1)[i] = u32x4{0, 0, 0, 0};
   issue_k(0, lds_k0);
   wait_k(true);  // Q and K_0 landed
   read_q();
   barrier();     // #0
   if (grp == 0) {
     // group A: period j = GEMM(j), softmax(j)
-    auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
+    auto tile = [&](int j, auto buf, auto kind) __attribute__((always_inline)) {
       // start of period j: the copies go out inside the GEMM phase
-      gemm_phase(j, buf, [&]() __attribute__((always_inline)) { issue_k_next_inline(j, buf); });
+      gemm_phase(j, buf, [&]() __attribute__((always_inline)) { issue_k_next_inline(j, buf); }, kind);
       softmax(j);
       wait_k(j + 1 < n_kt);
       barrier();                // end of period j
     };
-    int j = 0;
-    for (; j + 1 < n_kt; j += 2) {
-      tile(j, I0{});
-      tile(j + 1, I1{});
+    tile(0, I0{}, I1{});
+    int j = 1;
+    for (; j + 1 < j_end; j += 2) {
+      tile(j, I1{}, I0{});
+      tile(j + 1, I0{}, I0{});
     }
-    if (j < n_kt) {
-      tile(j, I0{});
+    if (j < j_end) {
+      tile(j, I1{}, I0{});
       ++j;
     }
-    // P.V of the last tile
-    if (j & 1) gemm_phase(j, I1{}, no_copies);
-    else gemm_phase(j, I0{}, no_copies);
+    // period j_end: P.V of the wave's last tile; for j_end < n_kt (causal,
+    // rows above the workgroup's last) the wave then only copies its share
+    // of the tiles and meets the barriers until the workgroup is done
+    if (j < n_kt) {
+      if (j & 1) issue_k_next(j, I1{});
+      else issue_k_next(j, I0{});
+    }
+    if (j & 1) gemm_phase(j, I1{}, no_copies, I2{});
+    else gemm_phase(j, I0{}, no_copies, I2{});
+    for (; j < n_kt; ++j) {
+      if (j > j_end) {
+        if (j & 1) issue_k_next(j, I1{});
+        else issue_k_next(j, I0{});
+      }
+      wait_k(true);
+      barrier();                // end of period j
+    }
   } else {
     // group B: period j = softmax(j-1), GEMM(j)
     issue_k_next(0, I0{});      // start of period 0
-    auto tile = [&](int j, auto buf) __attribute__((always_inline)) {
-      gemm_phase(j, buf, no_copies);
+    auto tile = [&](int j, auto buf, auto kind) __attribute__((always_inline)) {
+      gemm_phase(j, buf, no_copies, kind);
       wait_k(j + 1 < n_kt);
       barrier();                // end of period j
       if constexpr (decltype(buf)::value == 0)
@@ -779,18 +797,26 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
         issue_k_next(j + 1, I0{});
       softmax(j);
     };
-    int j = 0;
-    for (; j + 1 < n_kt; j += 2) {
-      tile(j, I0{});
-      tile(j + 1, I1{});
+    tile(0, I0{}, I1{});
+    int j = 1;
+    for (; j + 1 < j_end; j += 2) {
+      tile(j, I1{}, I0{});
+      tile(j + 1, I0{}, I0{});
     }
-    if (j < n_kt) {
-      tile(j, I0{});
+    if (j < j_end) {
+      tile(j, I1{}, I0{});
       ++j;
     }
-    // P.V of the last tile
-    if (j & 1) gemm_phase(j, I1{}, no_copies);
-    else gemm_phase(j, I0{}, no_copies);
+    // period j_end: P.V of the wave's last tile, then (j_end < n_kt) copies
+    // and barriers only
+    if (j & 1) gemm_phase(j, I1{}, no_copies, I2{});
+    else gemm_phase(j, I0{}, no_copies, I2{});
+    for (; j < n_kt; ++j) {
+      wait_k(true);
+      barrier();                // end of period j
+      if (j & 1) issue_k_next(j + 1, I0{});  // start of period j+1
+      else issue_k_next(j + 1, I1{});
+    }
   }
 
   // ---- epilogue: O = O^T / l, LSE = scale*m + ln(l) ------------------------
