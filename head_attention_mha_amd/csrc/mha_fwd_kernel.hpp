@@ -29,8 +29,9 @@
 //
 // gfx950 choices (not from the pages):
 // * Ping-pong of two wave groups. Waves 0-3 and 4-7 each alternate a GEMM
-//   phase (P.V of the previous tile and S^T of the current tile, 32 MFMAs)
-//   and a softmax phase (VALU), the second group half a period behind the
+//   phase (P.V of the previous tile and S^T of the current tile, 32 MFMAs;
+//   a wave's first phase has no P.V, its last no S^T) and a softmax phase
+//   (VALU), the second group half a period behind the
 //   first: every SIMD holds one wave of each group, so one issues MFMAs
 //   while the other runs its softmax. One workgroup barrier per key tile
 //   (period) covers the reuse of the K and V buffers; within a period the
@@ -557,14 +558,13 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
       }
       return a;
     };
-    // the first operand reads and the copies go out on every wave (a wave
-    // past its rows discards the operands), so the copies appear once
+    // the first operand reads, then the copies
     u32x4 buf[kAhead];
 #pragma unroll
     for (int n = N0; n < N0 + kAhead && n < NE; ++n) buf[n % kAhead] = load_op(n);
     copies();
     PinInterleave<N0, NPV, NE, kAhead>::pin_preload();
-    if (j > j_end) return;  // wave-uniform: past this wave's rows
+    if (j > j_end) return;  // guard (wave-uniform): the loops stop at j_end
     if constexpr (NE > NPV) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void mha_fwd_kernel(Params p) {
 
   // Softmax phase of tile j: mask, running max, exp, row sum, P^T fragments.
   auto softmax = [&](int j) __attribute__((always_inline)) {
-    if (j >= j_end) return;
+    if (j >= j_end) return;  // guard: the loops call it for j < j_end only
     const int k0 = j * BK;
     if (j >= jm) {
       // the empty asm keeps the compiler from turning this rarely taken,
