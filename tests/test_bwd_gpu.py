@@ -20,6 +20,7 @@ import pytest
 import oracle
 import workloads as wl
 from parity_bwd import assert_bwd_parity, compare_head, head_reference, merge_stats, unit_roundoff
+from ragged import case_id, ragged_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -180,6 +181,17 @@ def test_bwd_shapes(torch_mod, mha, case):
         # keys no query sees: exactly zero
         assert not np.any(wl.bits_to_f32(gk[:, Nq:], dtype)) and not np.any(
             wl.bits_to_f32(gv[:, Nq:], dtype))
+
+
+# 32-row query tiles and 32-key blocks (pairs of them at d = 128), 256-row
+# workgroups
+@pytest.mark.parametrize("case", ragged_cases(10, 4048, [32, 64, 96, 128, 160, 256], 600), ids=case_id)
+def test_bwd_random_ragged_shapes(torch_mod, mha, case):
+    B, H, Nq, Nk, d, dtype, causal = case
+    qb, kb, vb = wl.random_inputs(B, H, Nq, Nk, d, dtype, seed=8000 + 3 * Nq + Nk)
+    gb = wl.random_grad(B, H, Nq, d, dtype, seed=9000 + 3 * Nq + Nk)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    check_problem(torch_mod, mha, qb, kb, vb, gb, dtype, causal, scale, label=str(case))
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])

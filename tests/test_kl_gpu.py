@@ -20,6 +20,7 @@ import pytest
 
 import oracle
 import workloads as wl
+from ragged import case_id, ragged_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -114,6 +115,15 @@ SHAPES = [
 def test_kl_shapes(torch_mod, mha, case):
     B, H, Nq, Nk, d, dtype, causal = case
     q1, k1, q2, k2 = _inputs(B, H, Nq, Nk, d, dtype, 700 + Nq + Nk)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    check(torch_mod, mha, q1, k1, q2, k2, dtype, causal, scale, label=str(case))
+
+
+# 64-key tiles and 256-row workgroups
+@pytest.mark.parametrize("case", ragged_cases(10, 6072, [64, 128, 256, 512], 700), ids=case_id)
+def test_kl_random_ragged_shapes(torch_mod, mha, case):
+    B, H, Nq, Nk, d, dtype, causal = case
+    q1, k1, q2, k2 = _inputs(B, H, Nq, Nk, d, dtype, 10000 + 3 * Nq + Nk)
     scale = float(np.float32(1 / math.sqrt(d)))
     check(torch_mod, mha, q1, k1, q2, k2, dtype, causal, scale, label=str(case))
 

@@ -14,6 +14,7 @@ import oracle
 import workloads as wl
 from oracle_rows import attention_fwd_rows
 from parity import assert_parity, compare, report
+from ragged import case_id, ragged_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -117,30 +118,8 @@ def test_edge_shapes(torch_mod, mha, case):
     check_against_oracle(torch_mod, mha, qb, kb, vb, dtype, causal, scale, None, str(case))
 
 
-def _ragged_cases(n=16, seed=2024):
-    """Seeded shapes whose lengths sit on, just below or just past the key
-    tile (64) and query tile (256) edges, or anywhere in between, with Nq
-    and Nk drawn independently, so the per-wave loop ends (a wave's last key
-    tile before, at or after the workgroup's last), single-tile rows and
-    causal Nq != Nk all occur."""
-    rng = np.random.default_rng(seed)
-
-    def length():
-        if rng.random() < 0.6:
-            edge = int(rng.choice([64, 128, 256, 512, 768]))
-            return max(1, edge + int(rng.integers(-1, 2)))
-        return int(rng.integers(1, 900))
-
-    cases = []
-    for _ in range(n):
-        d = int(rng.choice([64, 128]))
-        cases.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), length(), length(), d,
-                      str(rng.choice(["fp16", "bf16"])), bool(rng.random() < 0.6)))
-    return cases
-
-
-@pytest.mark.parametrize("case", _ragged_cases(), ids=lambda c: "B{}H{}q{}k{}d{}{}{}".format(
-    c[0], c[1], c[2], c[3], c[4], c[5], "c" if c[6] else ""))
+# 64-key and 256-query tiles
+@pytest.mark.parametrize("case", ragged_cases(16, 2024, [64, 128, 256, 512, 768], 900), ids=case_id)
 def test_random_ragged_shapes(torch_mod, mha, case):
     B, H, Nq, Nk, d, dtype, causal = case
     qb, kb, vb = wl.random_inputs(B, H, Nq, Nk, d, dtype, seed=7000 + 3 * Nq + Nk)
