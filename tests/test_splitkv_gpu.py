@@ -114,6 +114,35 @@ def test_splitkv_shapes(torch_mod, mha, case):
     check(torch_mod, mha, qb, kb, vb, dtype, causal, scale, n_splits, str(case))
 
 
+def _random_split_cases(n=10, seed=5096):
+    """Seeded decode shapes: Nq in 1..8, Nk on or next to a power-of-two
+    tile edge or anywhere below 6000, the split count drawn (empty splits
+    included) or left to the library."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        if rng.random() < 0.5:
+            nk = int(rng.choice([64, 256, 1024, 4096])) + int(rng.integers(-1, 2))
+        else:
+            nk = int(rng.integers(1, 6000))
+        splits = None if rng.random() < 0.4 else int(rng.integers(1, 65))
+        cases.append((int(rng.integers(1, 3)), int(rng.integers(1, 5)), int(rng.integers(1, 9)), nk,
+                      int(rng.choice([64, 128])), str(rng.choice(["fp16", "bf16"])),
+                      bool(rng.random() < 0.5), splits))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_split_cases(), ids=lambda c: "B{}H{}q{}k{}d{}{}{}s{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], "c" if c[6] else "", c[7]))
+def test_splitkv_random_shapes(torch_mod, mha, case):
+    B, H, Nq, Nk, d, dtype, causal, n_splits = case
+    qb, kb, vb = wl.random_inputs(B, H, Nq, Nk, d, dtype, seed=11000 + 3 * Nq + Nk)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    if n_splits is None:
+        n_splits = mha.mha_fwd_splitkv_splits(B, H, Nq, Nk)
+    check(torch_mod, mha, qb, kb, vb, dtype, causal, scale, n_splits, str(case))
+
+
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_splitkv_peaky_scores(torch_mod, mha, dtype):
     """Std-3 queries and keys at scale 0.25 make rows near one-hot, and the
