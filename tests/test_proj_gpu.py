@@ -118,6 +118,32 @@ def test_proj_shapes(torch_mod, mha, case):
     check(y, ob, wb, bb, dtype, label=str(case))
 
 
+def _random_proj_cases(n=10, seed=7120):
+    """Seeded shapes with token and feature counts on or next to the
+    256 x 256 tile edges or anywhere below a cap, 1-8 heads of 64 or 128.
+    Feature counts are multiples of 4, the entry point's documented
+    restriction, so their neighbours of an edge are 4 away."""
+    rng = np.random.default_rng(seed)
+
+    def length(cap, step):
+        if rng.random() < 0.5:
+            return max(step, int(rng.choice([256, 512, 768])) + step * int(rng.integers(-1, 2)))
+        return step * int(rng.integers(1, cap // step))
+
+    return [(int(rng.integers(1, 4)), length(700, 1), int(rng.integers(1, 9)), int(rng.choice([64, 128])),
+             length(1200, 4), str(rng.choice(["fp16", "bf16"])), bool(rng.random() < 0.5))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("case", _random_proj_cases(), ids=lambda c: "B{}q{}H{}d{}E{}{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], "b" if c[6] else ""))
+def test_proj_random_shapes(torch_mod, mha, case):
+    B, Nq, H, d, E, dtype, bias = case
+    ob, wb, bb = _inputs(B, Nq, H, d, E, dtype, 12000 + 3 * Nq + E, bias)
+    y = run_proj(torch_mod, mha, ob, wb, bb, dtype)
+    check(y, ob, wb, bb, dtype, label=str(case))
+
+
 @pytest.mark.parametrize("name", list(wl.PROJ_WORKLOADS))
 def test_proj_workloads(torch_mod, mha, name):
     w = wl.PROJ_WORKLOADS[name]
