@@ -249,8 +249,12 @@ def test_bwd_workload(torch_mod, mha, name):
 
 
 # ------------------------------------------------------------ end to end
+# plus seeded ragged shapes; the RMS bar needs nonzero reference gradients,
+# so one query or one key (where dS is zero in exact arithmetic) is left out
 @pytest.mark.parametrize("case", [(2, 4, 333, 333, 128, "bf16", True),
-                                  (1, 8, 200, 450, 64, "fp16", False)])
+                                  (1, 8, 200, 450, 64, "fp16", False)] +
+                         [c for c in ragged_cases(8, 4049, [32, 64, 96, 128, 160, 256], 600)
+                          if c[2] > 1 and c[3] > 1], ids=case_id)
 def test_bwd_after_gpu_forward(torch_mod, mha, case):
     """The GPU forward's O and LSE feed the GPU backward. The element bound
     needs the exact deviation of the kernel's inputs, which here come from the
